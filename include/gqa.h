@@ -1,0 +1,134 @@
+/*
+ * libgqa -- fused causal grouped-query attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (forward), for batch b, query head h and query position i:
+ *
+ *     g      = h / (H / G)                              query heads share kv heads in
+ *                                                       contiguous groups
+ *     s_ij   = scale * sum_c Q[b,h,i,c] * K[b,g,j,c]    scaled dot product, scale = 1/sqrt(D)
+ *     vis_ij = j <= i  and  (window == 0  or  j > i - window  or  j < num_sinks)
+ *     P_ij   = exp(s_ij - lse_i) over visible j, 0 elsewhere
+ *     lse_i  = log sum_{visible j} exp(s_ij)             natural log of the scaled scores
+ *     O[b,h,i,:] = sum_j P_ij V[b,g,j,:]
+ *
+ * Sources.  The scaled-dot-product causal softmax, the P.V product and the grouped head
+ * map are those of "nx_f32_gqa_gate.nx source" (nishifamily.com): its header comment
+ * states the causal scaled softmax attention, and its test T2 gives the map
+ * kv = qh / (H/G).  Window and sinks are the "SnapKitty Transformer 8B" model card's
+ * attention parameters (Model Specifications: Sliding Window, Attention Sinks; the
+ * FlashAttention Inference call flash_attention_fwd(Q, K, V, causal=True,
+ * sliding_window=..., num_sinks=...)).  The card gives only sizes; this library reads a
+ * window of W as "the W most recent keys, self included" and sinks as the first
+ * num_sinks key positions, exempt from the window but still causal.  The backward
+ * (recompute P from the saved log-sum-exp, dS = P * (dO V^T - D)) is the card's
+ * FlashAttention-3 backward entry in its Protected Inventions list, with
+ * D_i = sum_c dO[i,c] O[i,c] and loss L = <O, dO>.
+ *
+ * Layout.  All tensors are dense and row-major (contiguous, innermost index last):
+ *     Q, O, dO     [B][H][S][D]      element type from gqa_problem.dtype
+ *     K, V         [B][G][S][D]      same element type
+ *     lse, delta   [B][H][S]         fp32
+ *     dQ           [B][H][S][D]      fp32
+ *     dK, dV       [B][G][S][D]      fp32
+ * Query and key sequences have the same length S and the causal diagonal is j = i.
+ *
+ * Ownership.  The caller allocates and frees every buffer; device pointers must be
+ * device memory of the current HIP device, 16-byte aligned.  The library allocates
+ * nothing, never synchronises, and enqueues its kernels on `stream` (a hipStream_t
+ * passed as void*; NULL = the null stream) and returns.  Results are ready when the
+ * stream reaches that point.  The library keeps no state between calls, so calls on
+ * different streams may run concurrently if their output buffers do not overlap.
+ *
+ * Errors.  Every argument is validated on the host before any HIP call; a non-OK
+ * status means nothing was enqueued, except GQA_ERR_HIP (a launch failed: earlier
+ * kernels of the same call may have been enqueued).  No exception crosses this ABI.
+ * S == 0 or B == 0 is a valid empty problem and returns GQA_OK without a launch.
+ *
+ * Supported: D == 64; dtype GQA_BF16 and GQA_F16 (MFMA kernels) and GQA_F32 (fp32
+ * kernels for reference-precision runs).  causal == 0 means full (non-causal)
+ * attention and then requires window == 0 and num_sinks == 0.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1, /* null pointer, bad sizes or flags, misaligned pointer      */
+  GQA_ERR_UNSUPPORTED = 2, /* valid problem this build has no kernel for (e.g. D != 64)   */
+  GQA_ERR_WORKSPACE = 3,   /* backward workspace missing or smaller than required        */
+  GQA_ERR_HIP = 4          /* a HIP launch reported an error                             */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1, GQA_F16 = 2 } gqa_dtype;
+
+typedef struct gqa_problem {
+  int32_t B;         /* batch                                                          */
+  int32_t H;         /* query heads; H % G == 0                                        */
+  int32_t G;         /* key/value heads                                                */
+  int32_t S;         /* sequence length of queries and keys                            */
+  int32_t D;         /* head dimension (64)                                            */
+  float scale;       /* softmax scale applied to q.k; finite and > 0 (1/sqrt(D))       */
+  int32_t causal;    /* 1: key j visible to query i only if j <= i; 0: full attention  */
+  int32_t window;    /* 0: no window; W > 0: also require j > i - W (unless a sink)     */
+  int32_t num_sinks; /* keys j < num_sinks ignore the window (still causal); >= 0      */
+  int32_t dtype;     /* gqa_dtype of Q, K, V, O and dO                                 */
+} gqa_problem;
+
+/* ABI version of the loaded library (GQA_ABI_VERSION it was built with). */
+int gqa_abi_version(void);
+
+/* Static, human-readable name of a gqa_status value; never NULL. */
+const char* gqa_status_str(int status);
+
+/* Number of visible (query, key) pairs of one (batch, head), computed on the host from
+ * the visibility rule above; -1 if the problem is invalid.  The algorithmic work of the
+ * forward is 4 * D * pairs * B * H flop (Q K^T and P V), of the backward
+ * 10 * D * pairs * B * H flop (S, dP, dV, dK, dQ). */
+int64_t gqa_visible_pairs(const gqa_problem* p);
+
+/* Forward.  Reads Q, K, V; writes O (dtype) and lse (fp32, natural log, of the scaled
+ * scores).  lse is what the backward needs to recompute P. */
+int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o,
+                 float* lse, void* stream);
+
+/* Bytes of device workspace gqa_attn_bwd needs (the fp32 delta vector [B][H][S]),
+ * rounded up to 256; 0 for an invalid or empty problem. */
+size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p);
+
+/* Backward of L = <O, dO>: dQ, dK, dV (fp32, overwritten, not accumulated into) from the
+ * forward's inputs, its output O and its lse.  Runs gqa_attn_bwd_preprocess into the
+ * workspace, then gqa_attn_bwd_dkdv and gqa_attn_bwd_dq, on one stream.  Deterministic:
+ * no floating-point atomics, so repeated calls give bit-identical results. */
+int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* d_o, float* dq, float* dk,
+                 float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward step 1: delta[b,h,i] = sum_c dO[b,h,i,c] * O[b,h,i,c], accumulated in fp32. */
+int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* d_o,
+                            float* delta, void* stream);
+
+/* Backward step 2: dK and dV.  Each kv head's gradient sums over the H/G query heads that
+ * read it; the sum stays in registers (no atomics). */
+int gqa_attn_bwd_dkdv(const gqa_problem* p, const void* q, const void* k, const void* v,
+                      const float* lse, const void* d_o, const float* delta, float* dk,
+                      float* dv, void* stream);
+
+/* Backward step 3: dQ, one pass per query tile over its visible key tiles. */
+int gqa_attn_bwd_dq(const gqa_problem* p, const void* q, const void* k, const void* v,
+                    const float* lse, const void* d_o, const float* delta, float* dq,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

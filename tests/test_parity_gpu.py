@@ -1,0 +1,242 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU fp64 oracle.
+
+Tolerances (max abs / mean abs against the fp64 oracle):
+  fp32 inputs:  1e-4 max on O, lse, dQ, dK, dV
+  bf16 / f16:   2e-2 max and 2e-3 mean on O, dQ, dK, dV; 1e-3 max on lse
+Small cases are compared in full (several 64-row tiles and a ragged tail); the
+full-size workloads on sampled rows (forward) or whole sampled kv groups
+(backward), plus identities that hold at any size.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as ref
+import transformer_attention_07_amd as gqa
+from synth import WORKLOADS, Workload, make_inputs, sample_rows, sample_rows_c4
+
+pytestmark = pytest.mark.gpu
+
+F32_MAX = 1e-4
+LP_MAX, LP_MEAN = 2e-2, 2e-3
+LSE_MAX = 1e-3
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _err(name, got, want, max_tol, mean_tol=None):
+    err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    print(f"  {name}: max {mx:.3e} mean {mean:.3e}", flush=True)
+    assert np.isfinite(err).all(), f"{name}: non-finite values"
+    assert mx <= max_tol, f"{name}: max abs error {mx:.3e} > {max_tol}"
+    if mean_tol is not None:
+        assert mean <= mean_tol, f"{name}: mean abs error {mean:.3e} > {mean_tol}"
+
+
+def _tols(w: Workload):
+    return (F32_MAX, None, F32_MAX) if w.dtype == "f32" else (LP_MAX, LP_MEAN, LSE_MAX)
+
+
+def _kw(w: Workload):
+    return dict(causal=w.causal, window=w.window, num_sinks=w.num_sinks)
+
+
+def run_fwd(w, q, k, v):
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = gqa.gqa_attn_fwd(qd, kd, vd, scale=w.scale, **_kw(w))
+    torch.cuda.synchronize()
+    return (qd, kd, vd), o, lse
+
+
+def check_full(w: Workload, with_bwd=True):
+    print(f"[parity] {w}", flush=True)
+    q, k, v, do = make_inputs(w, with_do=with_bwd)
+    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    O, L = ref.forward(q, k, v, scale=w.scale, **_kw(w))
+    mx, mean, lmx = _tols(w)
+    _err("O", _np(o), O, mx, mean)
+    _err("lse", _np(lse), L, lmx)
+    if not with_bwd:
+        return
+    dod = do.cuda()
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, **_kw(w))
+    torch.cuda.synchronize()
+    dQ, dK, dV = ref.backward(q, k, v, do, scale=w.scale, **_kw(w))
+    _err("dQ", _np(dq), dQ, mx, mean)
+    _err("dK", _np(dk), dK, mx, mean)
+    _err("dV", _np(dv), dV, mx, mean)
+
+
+def test_c1_fp32_fwd_bwd():
+    check_full(WORKLOADS["c1"])
+
+
+SMALL = [
+    # (B, H, G, S, causal, window, sinks)
+    (1, 4, 2, 200, True, 0, 0),
+    (2, 8, 2, 333, True, 0, 0),
+    (1, 8, 8, 130, True, 0, 0),      # H == G
+    (1, 6, 2, 257, True, 0, 0),      # three heads per kv head
+    (1, 4, 1, 190, True, 0, 0),      # one kv head
+    (1, 4, 2, 300, False, 0, 0),     # full attention
+    (1, 8, 2, 700, True, 100, 50),   # window + sinks, nothing tile aligned
+    (1, 8, 2, 640, True, 64, 64),    # window + sinks on tile edges
+    (1, 4, 2, 520, True, 1, 0),      # each query sees only itself
+    (1, 4, 2, 520, True, 1, 3),
+    (1, 4, 2, 300, True, 300, 10),   # window >= S: plain causal
+    (1, 4, 2, 300, True, 50, 400),   # sinks >= S: plain causal
+    (1, 2, 2, 1, True, 0, 0),        # single token
+    (1, 4, 2, 65, True, 0, 0),
+    (1, 16, 2, 1100, True, 300, 130),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}G{}S{}c{}W{}N{}".format(*c))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_full(case, dtype):
+    B, H, G, S, causal, W, NS = case
+    w = Workload("small", B=B, H=H, G=G, S=S, dtype=dtype, causal=causal, window=W, num_sinks=NS,
+                 direction="fwd+bwd", seed=4321 + S + H)
+    check_full(w)
+
+
+def test_small_f16():
+    check_full(Workload("small_f16", B=2, H=8, G=2, S=333, dtype="f16", window=90, num_sinks=20,
+                        direction="fwd+bwd", seed=77))
+
+
+def _check_sampled_rows(w, rows_bhi, q, k, v, o, lse):
+    mx, mean, lmx = _tols(w)
+    got_o, got_l, want_o, want_l = [], [], [], []
+    o_c, lse_c = o.float().cpu(), lse.cpu()
+    trip = np.asarray(rows_bhi)
+    for (b, h) in sorted(set(map(tuple, trip[:, :2].tolist()))):
+        sel = trip[(trip[:, 0] == b) & (trip[:, 1] == h), 2]
+        O, L = ref.forward_rows(q, k, v, b, h, sel, scale=w.scale, **_kw(w))
+        want_o.append(O)
+        want_l.append(L)
+        got_o.append(o_c[b, h, sel].numpy())
+        got_l.append(lse_c[b, h, sel].numpy())
+    print(f"  {len(trip)} sampled rows", flush=True)
+    _err("O", np.concatenate(got_o), np.concatenate(want_o), mx, mean)
+    _err("lse", np.concatenate(got_l), np.concatenate(want_l), lmx)
+
+
+def test_c2_full_size_sampled_rows():
+    w = WORKLOADS["c2"]
+    print(f"[parity] {w}", flush=True)
+    q, k, v, _ = make_inputs(w)
+    _, o, lse = run_fwd(w, q, k, v)
+    rows = sample_rows(w.B, w.H, w.S, 2048, w.seed, forced_rows=(0, 1, 63, 64, 1023, 2047))
+    _check_sampled_rows(w, rows, q, k, v, o, lse)
+
+
+def test_c3_full_size_sampled_rows():
+    w = WORKLOADS["c3"]
+    print(f"[parity] {w}", flush=True)
+    q, k, v, _ = make_inputs(w)
+    _, o, lse = run_fwd(w, q, k, v)
+    rows = sample_rows(w.B, w.H, w.S, 1024, w.seed, forced_rows=(0, 1, 63, 64, 8191, 16383))
+    _check_sampled_rows(w, rows, q, k, v, o, lse)
+
+
+def test_c4_full_size_sampled_rows():
+    w = WORKLOADS["c4"]
+    print(f"[parity] {w}", flush=True)
+    q, k, v, _ = make_inputs(w)
+    _, o, lse = run_fwd(w, q, k, v)
+    _check_sampled_rows(w, sample_rows_c4(w), q, k, v, o, lse)
+
+
+def test_c5_full_size_bwd():
+    w = WORKLOADS["c5"]
+    print(f"[parity] {w}", flush=True)
+    q, k, v, do = make_inputs(w)
+    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    dod = do.cuda()
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, **_kw(w))
+    torch.cuda.synchronize()
+    mx, mean, _ = _tols(w)
+    hpg = w.H // w.G
+    # whole kv groups against the oracle (first group of batch 0, last group of the last batch)
+    for (b, g) in [(0, 0), (w.B - 1, w.G - 1)]:
+        print(f"  group b={b} g={g}", flush=True)
+        dQ, dK, dV = ref.backward_group(q, k, v, do, b, g, scale=w.scale, **_kw(w))
+        _err("dQ", _np(dq[b, g * hpg:(g + 1) * hpg]), dQ, mx, mean)
+        _err("dK", _np(dk[b, g]), dK, mx, mean)
+        _err("dV", _np(dv[b, g]), dV, mx, mean)
+    # identities at every group: sum_j dK = 0 and sum_j dV = sum over the group's dO
+    dk_sum = dk.double().sum(dim=2).cpu().numpy()
+    dv_sum = dv.double().sum(dim=2).cpu().numpy()
+    do_sum = do.double().reshape(w.B, w.G, hpg, w.S, w.D).sum(dim=(2, 3)).numpy()
+    print(f"  sum_j dK max {np.abs(dk_sum).max():.3e}; sum_j dV - sum dO max {np.abs(dv_sum - do_sum).max():.3e}",
+          flush=True)
+    assert np.abs(dk_sum).max() < 0.5
+    assert np.abs(dv_sum - do_sum).max() < 0.5
+
+
+def test_token0_and_gqa_map_on_gpu():
+    # token 0 sees only itself: O[b,h,0] is V[b,g(h),0] bit for bit, and every head of a
+    # group returns its kv head's row (heads {0,1} -> kv0, {2,3} -> kv1 when H=4, G=2)
+    w = Workload("t1", B=2, H=4, G=2, S=256, direction="fwd", seed=99)
+    q, k, v, _ = make_inputs(w)
+    _, o, lse = run_fwd(w, q, k, v)
+    oc = o.cpu()
+    for h, g in zip(range(4), [0, 0, 1, 1]):
+        assert torch.equal(oc[:, h, 0], v[:, g, 0])
+
+
+def test_backward_is_deterministic():
+    w = Workload("det", B=2, H=8, G=2, S=777, window=200, num_sinks=30, direction="fwd+bwd", seed=5)
+    q, k, v, do = make_inputs(w)
+    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    dod = do.cuda()
+    r1 = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, **_kw(w))
+    r2 = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, **_kw(w))
+    o2, lse2 = gqa.gqa_attn_fwd(qd, kd, vd, **_kw(w))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_substeps_match_combined_backward():
+    w = Workload("sub", B=1, H=8, G=2, S=300, direction="fwd+bwd", seed=6)
+    q, k, v, do = make_inputs(w)
+    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    dod = do.cuda()
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod)
+    delta = gqa.gqa_attn_bwd_preprocess(o, dod)
+    dk2, dv2 = gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta)
+    dq2 = gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    # delta against its definition in fp64
+    want = (o.double() * dod.double()).sum(-1)
+    assert (delta.double() - want).abs().max().item() < 1e-4
+
+
+def test_empty_problem():
+    q = torch.empty(1, 4, 0, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = gqa.gqa_attn_fwd(q, k, k)
+    assert o.shape == q.shape and lse.shape == (1, 4, 0)
+
+
+def test_autograd_wrapper():
+    w = Workload("ag", B=1, H=4, G=2, S=150, window=40, num_sinks=8, direction="fwd+bwd", seed=8)
+    q, k, v, do = make_inputs(w)
+    qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o, lse = gqa.gqa_attention(qd, kd, vd, causal=True, sliding_window=w.window, num_sinks=w.num_sinks)
+    o.backward(do.cuda())
+    dQ, dK, dV = ref.backward(q, k, v, do, window=w.window, num_sinks=w.num_sinks)
+    # gradients come back in the input dtype (bf16): allow its rounding on top
+    _err("dQ", _np(qd.grad), dQ, LP_MAX + 2e-2, LP_MEAN)
+    _err("dK", _np(kd.grad), dK, LP_MAX + 2e-2, LP_MEAN)
+    _err("dV", _np(vd.grad), dV, LP_MAX + 2e-2, LP_MEAN)

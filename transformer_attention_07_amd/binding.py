@@ -1,0 +1,267 @@
+"""Python binding of libgqa (ctypes).  Argument marshalling only: shapes, dtypes and
+device pointers of torch tensors are passed to the C-ABI, and every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device memory
+and the current stream.
+
+The functions carry the C-ABI's names (``gqa_attn_fwd``, ``gqa_attn_bwd``,
+``gqa_attn_bwd_preprocess``, ``gqa_attn_bwd_dkdv``, ``gqa_attn_bwd_dq``,
+``gqa_visible_pairs``) and raise ``GqaError`` on a non-OK status.  The library
+must be built (``transformer_attention_07_amd.build``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
+GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
+_DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_F16}
+
+EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",
+            "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
+            "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq")
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)}")
+        self.status = status
+
+
+class gqa_problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("D", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_sinks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libgqa.so (once) and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libgqa.so is not built ({_LIB_PATH}); run "
+                          "`python -m transformer_attention_07_amd.build` first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(gqa_problem)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    lib.gqa_abi_version.restype = ctypes.c_int
+    lib.gqa_abi_version.argtypes = []
+    lib.gqa_status_str.restype = ctypes.c_char_p
+    lib.gqa_status_str.argtypes = [ctypes.c_int]
+    lib.gqa_visible_pairs.restype = ctypes.c_int64
+    lib.gqa_visible_pairs.argtypes = [P]
+    lib.gqa_attn_fwd.restype = ctypes.c_int
+    lib.gqa_attn_fwd.argtypes = [P, vp, vp, vp, vp, fp, vp]
+    lib.gqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_attn_bwd_workspace_bytes.argtypes = [P]
+    lib.gqa_attn_bwd.restype = ctypes.c_int
+    lib.gqa_attn_bwd.argtypes = [P, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.gqa_attn_bwd_preprocess.restype = ctypes.c_int
+    lib.gqa_attn_bwd_preprocess.argtypes = [P, vp, vp, fp, vp]
+    lib.gqa_attn_bwd_dkdv.restype = ctypes.c_int
+    lib.gqa_attn_bwd_dkdv.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
+    lib.gqa_attn_bwd_dq.restype = ctypes.c_int
+    lib.gqa_attn_bwd_dq.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, vp]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return library().gqa_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return library().gqa_abi_version()
+
+
+def make_problem(B, H, G, S, D=64, scale=None, causal=True, window=0, num_sinks=0,
+                 dtype=torch.bfloat16) -> gqa_problem:
+    code = dtype if isinstance(dtype, int) else _DTYPES.get(dtype, -1)
+    return gqa_problem(int(B), int(H), int(G), int(S), int(D),
+                       float(1.0 / math.sqrt(D) if scale is None else scale),
+                       int(bool(causal)) if causal in (True, False, 0, 1) else int(causal),
+                       int(window), int(num_sinks), int(code))
+
+
+def _check(status: int, what: str):
+    if status != GQA_OK:
+        raise GqaError(status, what)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _problem_from(q, k, causal, window, num_sinks, scale) -> gqa_problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,H,S,D] and k/v [B,G,S,D]")
+    B, H, S, D = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return make_problem(B, H, k.shape[1], S, D, scale, causal, window, num_sinks, q.dtype)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def gqa_visible_pairs(S, causal=True, window=0, num_sinks=0) -> int:
+    """Visible (query, key) pairs of one head (computed by the library on the host)."""
+    n = library().gqa_visible_pairs(ctypes.byref(make_problem(1, 1, 1, S, 64, None, causal, window,
+                                                              num_sinks, GQA_BF16)))
+    if n < 0:
+        raise GqaError(GQA_ERR_INVALID_ARG, "gqa_visible_pairs")
+    return int(n)
+
+
+def gqa_attn_fwd(q, k, v, causal=True, window=0, num_sinks=0, scale=None, out=None, lse=None,
+                 stream=None):
+    """O [B,H,S,D] (q.dtype) and lse [B,H,S] (fp32) of causal grouped-query attention."""
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype=q.dtype, device=q.device)
+    _need(v, "v", shape=k.shape)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _need(out, "out", dtype=q.dtype, shape=q.shape, device=q.device)
+    _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    _check(library().gqa_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  _stream(stream)), "gqa_attn_fwd")
+    return out, lse
+
+
+def gqa_attn_bwd_workspace_bytes(q, k, causal=True, window=0, num_sinks=0, scale=None) -> int:
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    return int(library().gqa_attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def _grad_buffers(q, k, dq, dk, dv):
+    f32 = torch.float32
+    dq = torch.empty(q.shape, dtype=f32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=f32, device=q.device) if dv is None else dv
+    _need(dq, "dq", dtype=f32, shape=q.shape, device=q.device)
+    _need(dk, "dk", dtype=f32, shape=k.shape, device=q.device)
+    _need(dv, "dv", dtype=f32, shape=k.shape, device=q.device)
+    return dq, dk, dv
+
+
+def _check_bwd_inputs(q, k, v, o, lse, d_o):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _need(t, n, dtype=q.dtype, device=q.device)
+    _need(v, "v", shape=k.shape)
+    _need(o, "o", shape=q.shape)
+    _need(d_o, "d_o", shape=q.shape)
+    _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+
+
+def gqa_attn_bwd(q, k, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale=None, dq=None,
+                 dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV (fp32) of L = <O, dO>, from the forward's O and lse."""
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q, k, v, o, lse, d_o)
+    dq, dk, dv = _grad_buffers(q, k, dq, dk, dv)
+    nbytes = int(library().gqa_attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(library().gqa_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "gqa_attn_bwd")
+    return dq, dk, dv
+
+
+def gqa_attn_bwd_preprocess(o, d_o, delta=None, stream=None):
+    """delta [B,H,S] fp32 = rowsum(dO * O)."""
+    _need(o, "o", device=o.device)
+    _need(d_o, "d_o", dtype=o.dtype, shape=o.shape, device=o.device)
+    B, H, S, D = o.shape
+    if delta is None:
+        delta = torch.empty((B, H, S), dtype=torch.float32, device=o.device)
+    _need(delta, "delta", dtype=torch.float32, shape=(B, H, S), device=o.device)
+    p = make_problem(B, H, 1, S, D, None, True, 0, 0, o.dtype)
+    _check(library().gqa_attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(d_o), _ptr(delta),
+                                             _stream(stream)), "gqa_attn_bwd_preprocess")
+    return delta
+
+
+def gqa_attn_bwd_dkdv(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks=0, scale=None,
+                      dk=None, dv=None, stream=None):
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q, k, v, q, lse, d_o)
+    _need(delta, "delta", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    _, dk, dv = _grad_buffers(q, k, q.new_empty(q.shape, dtype=torch.float32), dk, dv)
+    _check(library().gqa_attn_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
+                                       _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)),
+           "gqa_attn_bwd_dkdv")
+    return dk, dv
+
+
+def gqa_attn_bwd_dq(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks=0, scale=None, dq=None,
+                    stream=None):
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q, k, v, q, lse, d_o)
+    _need(delta, "delta", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(dq, "dq", dtype=torch.float32, shape=q.shape, device=q.device)
+    _check(library().gqa_attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
+                                     _ptr(delta), _ptr(dq), _stream(stream)), "gqa_attn_bwd_dq")
+    return dq
+
+
+class GqaAttention(torch.autograd.Function):
+    """Autograd wrapper: forward through gqa_attn_fwd, backward through gqa_attn_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, window, num_sinks, scale):
+        o, lse = gqa_attn_fwd(q, k, v, causal, window, num_sinks, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (causal, window, num_sinks, scale)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, d_o, d_lse):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, window, num_sinks, scale = ctx.cfg
+        dq, dk, dv = gqa_attn_bwd(q, k, v, o, lse, d_o.contiguous().to(q.dtype), causal, window,
+                                  num_sinks, scale)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
+
+
+def gqa_attention(q, k, v, causal=True, sliding_window=0, num_sinks=0, scale=None):
+    """(O, lse) with autograd; the model card's call ``flash_attention_fwd(Q, K, V, causal=True,
+    sliding_window=..., num_sinks=...)`` maps to ``gqa_attention(q, k, v, ...)``.  The
+    gradient with respect to lse is not propagated."""
+    return GqaAttention.apply(q, k, v, causal, sliding_window, num_sinks, scale)

@@ -1,0 +1,238 @@
+// C-ABI of libgqa: argument validation, problem normalisation and kernel dispatch.
+// Everything is checked on the host before the first HIP call; see include/gqa.h.
+#include "gqa.h"
+
+#include <math.h>
+
+#include <climits>
+
+#include "gqa_internal.h"
+
+namespace {
+
+using gqa::BwdParams;
+using gqa::FwdParams;
+using gqa::MaskSpec;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Shape and flag checks shared by every entry point.
+int check_problem(const gqa_problem* p) {
+  if (p == nullptr) return GQA_ERR_INVALID_ARG;
+  if (p->B < 0 || p->S < 0 || p->H < 1 || p->G < 1 || p->D < 1) return GQA_ERR_INVALID_ARG;
+  if (p->H % p->G != 0) return GQA_ERR_INVALID_ARG;
+  if (!(isfinite(p->scale) && p->scale > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return GQA_ERR_INVALID_ARG;
+  if (p->window < 0 || p->num_sinks < 0) return GQA_ERR_INVALID_ARG;
+  if (p->causal == 0 && (p->window != 0 || p->num_sinks != 0)) return GQA_ERR_INVALID_ARG;
+  if (p->dtype != GQA_F32 && p->dtype != GQA_BF16 && p->dtype != GQA_F16) return GQA_ERR_INVALID_ARG;
+  if ((long long)p->B * p->H > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  if (p->D != gqa::kHeadDim) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+bool empty_problem(const gqa_problem* p) { return p->B == 0 || p->S == 0; }
+
+// The window and sink rule with the no-op cases folded away: a window of S or more
+// keys hides nothing, sinks only matter under a window, and more sinks than keys make
+// every key a sink.
+MaskSpec normalised_mask(const gqa_problem* p) {
+  MaskSpec m{p->S, p->causal, p->window, p->num_sinks};
+  if (m.window >= m.S) m.window = 0;
+  if (m.window == 0) m.sinks = 0;
+  if (m.sinks >= m.S) {
+    m.window = 0;
+    m.sinks = 0;
+  }
+  return m;
+}
+
+// Heads per workgroup for the kernels that give each of the 4 waves one 64-row tile of
+// one query head: as many heads of one kv group as divide H/G (up to 4), the remaining
+// waves taking further row tiles of the same heads.
+void row_decomposition(const gqa_problem* p, int* hpw, int* qpw, int* n_qblk) {
+  const int hpg = p->H / p->G;
+  *hpw = (hpg % 4 == 0) ? 4 : (hpg % 2 == 0) ? 2 : 1;
+  *qpw = 4 / *hpw;
+  *n_qblk = (p->S + gqa::kTile * *qpw - 1) / (gqa::kTile * *qpw);
+}
+
+int grid_ok(long long blocks) { return blocks > 0 && blocks <= INT_MAX; }
+
+int fill_bwd(const gqa_problem* p, BwdParams* bp) {
+  *bp = BwdParams{};
+  bp->B = p->B;
+  bp->H = p->H;
+  bp->G = p->G;
+  bp->S = p->S;
+  bp->scale = p->scale;
+  bp->scale_log2 = p->scale * kLog2e;
+  bp->mask = normalised_mask(p);
+  row_decomposition(p, &bp->hpw, &bp->qpw, &bp->n_qblk);
+  bp->n_kblk = (p->S + 4 * gqa::kTile - 1) / (4 * gqa::kTile);
+  if (!grid_ok((long long)bp->n_qblk * p->B * (p->H / bp->hpw))) return GQA_ERR_UNSUPPORTED;
+  if (!grid_ok((long long)bp->n_kblk * p->B * p->G)) return GQA_ERR_UNSUPPORTED;
+  if (!grid_ok((long long)p->B * p->H * ((p->S + 63) / 64))) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char* gqa_status_str(int status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: valid problem without a kernel in this build";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: kernel launch failed";
+    default: return "unknown gqa_status";
+  }
+}
+
+int64_t gqa_visible_pairs(const gqa_problem* p) {
+  const int rc = check_problem(p);
+  if (rc == GQA_ERR_INVALID_ARG || p == nullptr) return -1;
+  const int64_t S = p->S;
+  if (S == 0) return 0;
+  const MaskSpec m = normalised_mask(p);
+  if (!m.causal) return S * S;
+  if (m.window == 0) return S * (S + 1) / 2;
+  const int64_t W = m.window, NS = m.sinks;  // 0 < W < S, NS < S
+  // sum_i min(i + 1, W): ramp to W, then W per row
+  int64_t pairs = W * (W + 1) / 2 + (S - W) * W;
+  // sinks older than the window: row i >= W adds min(NS, i - W + 1)
+  const int64_t n = S - W;
+  pairs += (n <= NS) ? n * (n + 1) / 2 : NS * (NS + 1) / 2 + (n - NS) * NS;
+  return pairs;
+}
+
+int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !o || !lse) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return GQA_ERR_INVALID_ARG;
+
+  FwdParams fp{};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.o = o;
+  fp.lse = lse;
+  fp.B = p->B;
+  fp.H = p->H;
+  fp.G = p->G;
+  fp.S = p->S;
+  fp.scale = p->scale;
+  fp.scale_log2 = p->scale * kLog2e;
+  fp.mask = normalised_mask(p);
+  row_decomposition(p, &fp.hpw, &fp.qpw, &fp.n_qblk);
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == GQA_F32) {
+    if (!grid_ok((long long)p->B * p->H * ((p->S + 63) / 64))) return GQA_ERR_UNSUPPORTED;
+    return hip_status(gqa::launch_fwd_f32(fp, s));
+  }
+  if (!grid_ok((long long)fp.n_qblk * p->B * (p->H / fp.hpw))) return GQA_ERR_UNSUPPORTED;
+  return hip_status(gqa::launch_fwd_mfma(fp, p->dtype, s));
+}
+
+size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p) {
+  if (check_problem(p) != GQA_OK || empty_problem(p)) return 0;
+  const size_t bytes = (size_t)p->B * p->H * p->S * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* d_o, float* delta, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!o || !d_o || !delta) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(d_o) || !aligned16(delta)) return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  bp.o = o;
+  bp.d_o = d_o;
+  bp.out_delta = delta;
+  const long long rows = (long long)p->B * p->H * p->S;
+  if (!grid_ok(rows / 16 + 1)) return GQA_ERR_UNSUPPORTED;
+  return hip_status(gqa::launch_bwd_preprocess(bp, p->dtype, (hipStream_t)stream));
+}
+
+int gqa_attn_bwd_dkdv(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
+                      const void* d_o, const float* delta, float* dk, float* dv, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dk || !dv) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dk = dk;
+  bp.dv = dv;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dkdv_f32(bp, s));
+  return hip_status(gqa::launch_bwd_dkdv_mfma(bp, p->dtype, s));
+}
+
+int gqa_attn_bwd_dq(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
+                    const void* d_o, const float* delta, float* dq, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dq) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dq))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dq = dq;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dq_f32(bp, s));
+  return hip_status(gqa::launch_bwd_dq_mfma(bp, p->dtype, s));
+}
+
+int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* d_o, float* dq, float* dk, float* dv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return GQA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  float* delta = (float*)workspace;
+  if ((rc = gqa_attn_bwd_preprocess(p, o, d_o, delta, stream)) != GQA_OK) return rc;
+  if ((rc = gqa_attn_bwd_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, stream)) != GQA_OK) return rc;
+  return gqa_attn_bwd_dq(p, q, k, v, lse, d_o, delta, dq, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Device helpers for the gfx950 MFMA attention kernels.
+//
+// Matrix core instruction: v_mfma_f32_32x32x16_{bf16,f16}, D[32x32] += A[32x16] B[16x32]
+// on one 64-lane wavefront.  Operand layout (A and B alike): lane l holds 8 consecutive
+// k-elements of row/column (l % 32), k-group (l / 32).  Accumulator layout: lane l holds
+// column (l % 32) and register r holds row 8*(r/4) + 4*(l/32) + (r%4).
+//
+// Two LDS tile layouts, both for 64 x 64 tiles of 16-bit elements (8 KiB):
+//   * row-major ("RM"): element (row, c) at row*128 + 16*((c/8) ^ (row%8)) + 2*(c%8).
+//     The 16-byte chunk is XOR-swizzled by the row so that 32 lanes reading the same
+//     chunk of 32 consecutive rows spread over all banks.  An A operand whose
+//     contraction index is the column (e.g. K for K Q^T) is one ds_read_b128 per lane.
+//   * transposed ("TR"): element (row, c) stored in LDS row c, so that an A operand
+//     whose contraction index is the tile row (e.g. V^T for V^T P^T) is contiguous.
+//     Within each group of 16 tile rows, row 8a + 4h + x (a, h in {0,1}, x in 0..3) is
+//     stored at position 8h + 4a + x.  With that order, the 8 elements a lane of
+//     k-group h reads for contraction step t of key block kb are exactly the tile rows
+//     held by accumulator registers 8t..8t+7 of a lane of the same k-group, so an
+//     accumulator (S^T, P^T, dS) feeds the next MFMA as a B operand straight from
+//     registers.  Chunks are swizzled by (c % 8) as in RM.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gqa_internal.h"
+
+namespace gqa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum { kDtF32 = 0, kDtBF16 = 1, kDtF16 = 2 };
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<kDtBF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<kDtF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Round two floats to the 16-bit element type (nearest even) and pack: a in the low half.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+
+template <>
+__device__ __forceinline__ uint32_t pack2<kDtBF16>(float a, float b) {
+  bf16x2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <>
+__device__ __forceinline__ uint32_t pack2<kDtF16>(float a, float b) {
+  f16x2 r = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 16-bit element (low half of w if hi == 0) to float.
+template <int DT>
+__device__ __forceinline__ float elem_to_f32(uint32_t w, int hi);
+
+template <>
+__device__ __forceinline__ float elem_to_f32<kDtBF16>(uint32_t w, int hi) {
+  return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16));
+}
+
+template <>
+__device__ __forceinline__ float elem_to_f32<kDtF16>(uint32_t w, int hi) {
+  uint16_t bits = (uint16_t)(hi ? (w >> 16) : (w & 0xffffu));
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value the lane (l ^ 32) holds, combined with ours: returns {ours, theirs} reduced by op.
+__device__ __forceinline__ float max_across_halves(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1]));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
+// ---- LDS layouts (byte offsets inside one 8 KiB tile) ----
+__device__ __forceinline__ int rm_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// TR layout: byte offset of the 16-byte chunk `chunk` (0..7) of LDS row `c`.
+__device__ __forceinline__ int tr_chunk_off(int c, int chunk) { return c * 128 + ((chunk ^ (c & 7)) << 4); }
+
+// A-operand reads.  RM: rows blk*32 + (l%32), contraction chunk 2*ks + (l/32).
+__device__ __forceinline__ u32x4 lds_rm_operand(const char* tile, int blk, int ks, int l32, int hl) {
+  return *(const u32x4*)(tile + rm_off(blk * 32 + l32, ks * 2 + hl));
+}
+// TR: LDS row (output row) blk*32 + (l%32); contraction tile rows 32*kb + 16*t + ..., the
+// 16-byte chunk 4*kb + 2*t + (l/32).
+__device__ __forceinline__ u32x4 lds_tr_operand(const char* tile, int blk, int kb, int t, int l32, int hl) {
+  const int c = blk * 32 + l32;
+  return *(const u32x4*)(tile + tr_chunk_off(c, kb * 4 + t * 2 + hl));
+}
+
+// ---- staging of a 64 x 64 tile from global memory ----
+// One "unit" = 4 consecutive tile rows r0..r0+3 (r0 % 4 == 0) times one 16-byte column
+// chunk dc (8 elements).  128 units cover a tile; a thread loads its unit into registers
+// (rows >= S read as zero), then writes it as RM and/or TR.
+struct Unit {
+  u32x4 x[4];
+};
+
+__device__ __forceinline__ void unit_load(Unit& u, const uint16_t* slab, int row0, int dc, int S) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = row0 + n;
+    if (row < S) {
+      u.x[n] = *(const u32x4*)(slab + (size_t)row * kHeadDim + dc * 8);
+    } else {
+      u.x[n] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void unit_store_rm(char* tile, const Unit& u, int r0, int dc) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) *(u32x4*)(tile + rm_off(r0 + n, dc)) = u.x[n];
+}
+
+__device__ __forceinline__ void unit_store_tr(char* tile, const Unit& u, int r0, int dc) {
+  const int q4 = r0 >> 2;                 // which group of 4 rows
+  const int chunk = (q4 >> 2) * 2 + (q4 & 1);  // 16-row group * 2 + h
+  const int a = (q4 >> 1) & 1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = dc * 8 + e;
+    const int w = e >> 1;
+    uint32_t lo, hi;
+    if (e & 1) {
+      lo = (u.x[0][w] >> 16) | (u.x[1][w] & 0xffff0000u);
+      hi = (u.x[2][w] >> 16) | (u.x[3][w] & 0xffff0000u);
+    } else {
+      lo = (u.x[0][w] & 0xffffu) | (u.x[1][w] << 16);
+      hi = (u.x[2][w] & 0xffffu) | (u.x[3][w] << 16);
+    }
+    *(u32x2*)(tile + tr_chunk_off(c, chunk) + a * 8) = u32x2{lo, hi};
+  }
+}
+
+// Row of the accumulator register r of this lane, inside a 32-row block.
+__device__ __forceinline__ int acc_row(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
+
+}  // namespace gqa

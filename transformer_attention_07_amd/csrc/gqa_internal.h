@@ -1,0 +1,165 @@
+// Internal declarations shared by the libgqa kernels and the C-ABI layer.
+//
+// Visibility rule (see include/gqa.h): key j is visible to query i iff
+//   j <= i  and  (window == 0  or  j > i - window  or  j < num_sinks)      (causal)
+//   always                                                               (non-causal)
+// restricted to 0 <= j < S.  The kernels work on square tiles of 64 keys; for a block
+// of query rows [q0, q1] the helpers below give the key tiles that contain at least one
+// visible key (all others are never loaded) and classify each tile as FULL (no mask
+// arithmetic needed) or PARTIAL (mask element by element).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kTile = 64;   // keys per key tile and query rows per wave tile
+constexpr int kHeadDim = 64;
+
+enum TileClass : int { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+struct MaskSpec {
+  int S;
+  int causal;
+  int window;
+  int sinks;
+};
+
+__host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+
+// Is key j visible to query i (both inside [0, S))?
+__host__ __device__ inline bool visible(const MaskSpec& m, int i, int j) {
+  if (j >= m.S) return false;
+  if (!m.causal) return true;
+  if (j > i) return false;
+  if (m.window > 0 && j <= i - m.window && j >= m.sinks) return false;
+  return true;
+}
+
+// Class of the block rows [q0, q1] x keys [k0, k1] (inclusive bounds, q1 < S assumed).
+// FULL is only returned when every pair is visible; PARTIAL is always a safe answer.
+__host__ __device__ inline int classify(const MaskSpec& m, int q0, int q1, int k0, int k1) {
+  if (k0 >= m.S) return kEmpty;
+  if (!m.causal) return (k1 < m.S) ? kFull : kPartial;
+  if (k0 > q1) return kEmpty;
+  if (m.window > 0) {
+    // union over the rows of the in-window keys is (q0 - W, q1]; sinks are [0, NS)
+    bool hits_window = k1 > q0 - m.window;
+    bool hits_sinks = k0 < m.sinks;
+    if (!hits_window && !hits_sinks) return kEmpty;
+  }
+  bool full = (k1 <= q0) && (k1 < m.S);
+  if (full && m.window > 0) full = (k0 > q1 - m.window) || (k1 < m.sinks);
+  return full ? kFull : kPartial;
+}
+
+// Key tiles a block of query rows [q0, q1] must visit, as at most two disjoint tile
+// ranges [a0, a1) and [b0, b1) (sink tiles, then window/causal tiles).
+struct TileRanges {
+  int a0, a1, b0, b1;
+  __host__ __device__ int count() const { return (a1 - a0) + (b1 - b0); }
+  __host__ __device__ int tile(int n) const { return n < (a1 - a0) ? a0 + n : b0 + (n - (a1 - a0)); }
+};
+
+__host__ __device__ inline TileRanges key_tiles_for_rows(const MaskSpec& m, int q0, int q1) {
+  TileRanges r{0, 0, 0, 0};
+  const int nt = (m.S + kTile - 1) / kTile;
+  if (!m.causal) {
+    r.b0 = 0;
+    r.b1 = nt;
+    return r;
+  }
+  const int last = q1 / kTile + 1;  // exclusive
+  if (m.window <= 0 || q0 - m.window + 1 <= 0) {
+    r.b0 = 0;
+    r.b1 = last;
+    return r;
+  }
+  const int wfirst = (q0 - m.window + 1) / kTile;
+  const int sink_end = (imin(m.sinks, q1 + 1) + kTile - 1) / kTile;  // exclusive
+  if (sink_end >= wfirst) {
+    r.b0 = 0;
+    r.b1 = last;
+  } else {
+    r.a0 = 0;
+    r.a1 = sink_end;
+    r.b0 = wfirst;
+    r.b1 = last;
+  }
+  return r;
+}
+
+// Query tiles that see at least one key of the key rows [k0, k1]: as two disjoint tile
+// ranges of query tiles (used by the dK/dV pass, which walks queries for fixed keys).
+__host__ __device__ inline TileRanges query_tiles_for_keys(const MaskSpec& m, int k0, int k1) {
+  TileRanges r{0, 0, 0, 0};
+  const int nt = (m.S + kTile - 1) / kTile;
+  if (!m.causal) {
+    r.b0 = 0;
+    r.b1 = nt;
+    return r;
+  }
+  const int first = k0 / kTile;  // queries i >= k0
+  if (m.window <= 0 || k0 < m.sinks) {
+    // sinks are seen by every later query; without a window every later query sees them
+    r.b0 = first;
+    r.b1 = nt;
+    return r;
+  }
+  // non-sink keys [k0, k1] are seen by queries i with j <= i < j + W, i.e. [k0, k1 + W - 1]
+  const int last_row = imin(m.S - 1, k1 + m.window - 1);
+  r.b0 = first;
+  r.b1 = last_row / kTile + 1;
+  return r;
+}
+
+// ---------------------------------------------------------------------------------
+// Kernel parameter blocks (passed by value).
+// ---------------------------------------------------------------------------------
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, G, S;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  MaskSpec mask;
+  int hpw;           // heads per workgroup (a divisor of H/G): waves 0..hpw-1 share rows
+  int qpw;           // 64-row query tiles per workgroup (4 / hpw)
+  int n_qblk;        // workgroup row blocks per head = ceil(S / (64 * qpw))
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  const float* delta;
+  float* out_delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, H, G, S;
+  float scale;
+  float scale_log2;
+  MaskSpec mask;
+  int hpw, qpw, n_qblk;  // dQ pass: same row decomposition as the forward
+  int n_kblk;            // dK/dV pass: 256-key blocks per kv head
+};
+
+// Launchers (return hipSuccess or the launch error).  Element type by dtype code.
+hipError_t launch_fwd_mfma(const FwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
+hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdParams& p, hipStream_t s);
+
+}  // namespace gqa
