@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused causal grouped-query attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic inputs
+already resident in HBM: the forward (O, lse), then the backward (delta,
+dK/dV, dQ) for an upstream gradient dO.  The default workload is the causal
+GQA shape B=4, H=32 query heads, G=8 kv heads, S=2048, d=64, bf16.
+
+Work is counted only on visible (query, key) pairs: forward 4*d*pairs*B*H flop
+(Q K^T and P V), backward 10*d*pairs*B*H flop (S, dP, dV, dK, dQ), where the
+pair count comes from the library's host-side rule.  The printed JSON line
+carries the step throughput, a roofline record for the dominant kernel (timed
+with HIP events on the stream the kernels run on) and the CPU fp64 oracle
+timed on a bounded sample of the same work on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+                       [--workload step|c2|c3|c4|c5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PFLOP/s dense)
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal GQA attention TFLOP/s (fwd, bwd) at d=64 + % of MI355X bf16 MFMA peak"
+KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_device.h", "gqa_internal.h"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step", choices=["step", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    return ap.parse_args()
+
+
+def workload(name):
+    from synth import WORKLOADS
+
+    if name == "step":
+        w = WORKLOADS["c2"].with_(name="step", direction="fwd+bwd")
+    elif name == "c5":
+        w = WORKLOADS["c5"].with_(direction="fwd+bwd")
+    else:
+        w = WORKLOADS[name]
+    return w
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_attention_07_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, wname):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
+    taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(f"{kernel}@{wname}")
+    if not ent or rec.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """The oracle, as it stands, on whole kv groups of the same workload until the
+    time budget is used: forward rows of every head of the group plus its backward."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.attention as ref
+    from transformer_attention_07_amd import gqa_visible_pairs
+
+    q, k, v, do = inputs
+    hpg = w.H // w.G
+    pairs = gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, num_sinks=w.num_sinks)
+    rows = np.arange(w.S)
+    t0 = time.perf_counter()
+    groups = 0
+    flop = 0.0
+    for b in range(w.B):
+        for g in range(w.G):
+            for h in range(g * hpg, (g + 1) * hpg):
+                ref.forward_rows(q, k, v, b, h, rows, **kw)
+            flop += 4.0 * w.D * pairs * hpg
+            if "bwd" in w.direction:
+                ref.backward_group(q, k, v, do, b, g, **kw)
+                flop += 10.0 * w.D * pairs * hpg
+            groups += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{groups} of {w.B * w.G} kv groups (all {hpg} heads each, "
+                      f"{'fwd+bwd' if 'bwd' in w.direction else 'fwd'}), {dt:.1f} s, fp64 numpy"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the attention path is built and measured on a "
+              "single MI355X (no collectives, no sharding); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_attention_07_amd as gqa
+    from synth import make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gqa.library()  # fail loudly if the HIP library is not built
+    w = workload(args.workload)
+    do_bwd = "bwd" in w.direction
+    print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+    q, k, v, do = make_inputs(w, with_do=do_bwd)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    dod = do.to(dev) if do_bwd else None
+    kw = dict(causal=w.causal, window=w.window, num_sinks=w.num_sinks, scale=w.scale)
+    o = torch.empty_like(qd)
+    o_lo = torch.empty_like(qd) if do_bwd else None  # O's rounding residual, kept for the backward
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    kernels = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq"] if do_bwd else [])
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        gqa.gqa_attn_fwd(qd, kd, vd, out=o, lse=lse, o_lo=o_lo, stream=stream, **kw)
+        mark(1)
+        if do_bwd:
+            gqa.gqa_attn_bwd_preprocess(o, dod, delta=delta, o_lo=o_lo, stream=stream)
+            mark(2)
+            gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta, dk=dk, dv=dv, stream=stream, **kw)
+            mark(3)
+            gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta, dq=dq, stream=stream, **kw)
+            mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:  # a plain copy of known size, for counter calibration
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {}
+    for i, name in enumerate(kernels):
+        per_kernel_ms[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
+    bh = w.B * w.H
+    flop = {"fwd": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0, "bwd_dkdv": 8.0 * w.D * pairs * bh,
+            "bwd_dq": 2.0 * w.D * pairs * bh}
+    elem = 2 if w.dtype in ("bf16", "f16") else 4
+    hbm_bytes = {"bwd_preprocess": 3.0 * bh * w.S * w.D * elem + bh * w.S * 4}  # O, o_lo, dO in; delta out
+    step_flop = flop["fwd"] + (10.0 * w.D * pairs * bh if do_bwd else 0.0)
+    value = step_flop / (ms_per_step * 1e-3) / 1e12
+
+    detail = {}
+    for name in kernels:
+        ms = per_kernel_ms[name]
+        d = {"ms": round(ms, 5)}
+        if flop[name] > 0:
+            t = flop[name] / (ms * 1e-3) / 1e12
+            d.update(tflops=round(t, 1), pct_peak=round(100 * t / MFMA_BF16_PEAK_TFLOPS, 1))
+        else:
+            d.update(gbs=round(hbm_bytes[name] / (ms * 1e-3) / 1e9, 1))
+        detail[name] = d
+    fwd_tflops = flop["fwd"] / (per_kernel_ms["fwd"] * 1e-3) / 1e12
+    if do_bwd:
+        bwd_ms = sum(per_kernel_ms[n] for n in kernels[1:])
+        detail["bwd_total"] = {"ms": round(bwd_ms, 5),
+                               "tflops": round(10.0 * w.D * pairs * bh / (bwd_ms * 1e-3) / 1e12, 1)}
+    detail["fwd_tflops"] = round(fwd_tflops, 1)
+
+    dominant = max((n for n in kernels if flop[n] > 0), key=lambda n: per_kernel_ms[n])
+    ach = flop[dominant] / (per_kernel_ms[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": load_traffic(dominant, w.name)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, (q, k, v, do), args.cpu_seconds)
+
+    wl = (f"causal GQA {'fwd+bwd' if do_bwd else 'fwd'}, B={w.B} H={w.H} G={w.G} S={w.S} d={w.D}"
+          + (f" window={w.window} sinks={w.num_sinks}" if w.window else "") + f", {w.dtype}")
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": wl, "B": w.B, "H": w.H, "G": w.G, "S": w.S, "D": w.D, "causal": w.causal,
+                   "window": w.window, "num_sinks": w.num_sinks, "visible_pairs_per_head": pairs,
+                   "flop_per_step": step_flop, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernels": detail,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

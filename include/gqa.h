@@ -96,25 +96,32 @@ const char* gqa_status_str(int status);
 int64_t gqa_visible_pairs(const gqa_problem* p);
 
 /* Forward.  Reads Q, K, V; writes O (dtype) and lse (fp32, natural log, of the scaled
- * scores).  lse is what the backward needs to recompute P. */
+ * scores).  lse is what the backward needs to recompute P.
+ * o_lo (optional, NULL to skip; must be NULL for GQA_F32): same shape and dtype as O,
+ * receives O's rounding residual (exact O minus the stored O, rounded to dtype).  Passed
+ * back to the backward it makes delta = rowsum(dO * O) carry about twice dtype's
+ * mantissa, which matters where many queries put large weight on the same keys (sinks):
+ * there each row's delta error is multiplied by a large P in dK. */
 int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o,
-                 float* lse, void* stream);
+                 void* o_lo, float* lse, void* stream);
 
 /* Bytes of device workspace gqa_attn_bwd needs (the fp32 delta vector [B][H][S]),
  * rounded up to 256; 0 for an invalid or empty problem. */
 size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p);
 
 /* Backward of L = <O, dO>: dQ, dK, dV (fp32, overwritten, not accumulated into) from the
- * forward's inputs, its output O and its lse.  Runs gqa_attn_bwd_preprocess into the
- * workspace, then gqa_attn_bwd_dkdv and gqa_attn_bwd_dq, on one stream.  Deterministic:
- * no floating-point atomics, so repeated calls give bit-identical results. */
+ * forward's inputs, its output O (and optionally o_lo, see gqa_attn_fwd; NULL if not
+ * kept) and its lse.  Runs gqa_attn_bwd_preprocess into the workspace, then
+ * gqa_attn_bwd_dkdv and gqa_attn_bwd_dq, on one stream.  Deterministic: no
+ * floating-point atomics, so repeated calls give bit-identical results. */
 int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v,
-                 const void* o, const float* lse, const void* d_o, float* dq, float* dk,
-                 float* dv, void* workspace, size_t workspace_bytes, void* stream);
+                 const void* o, const void* o_lo, const float* lse, const void* d_o, float* dq,
+                 float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward step 1: delta[b,h,i] = sum_c dO[b,h,i,c] * O[b,h,i,c], accumulated in fp32. */
-int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* d_o,
-                            float* delta, void* stream);
+/* Backward step 1: delta[b,h,i] = sum_c dO[b,h,i,c] * (O + o_lo)[b,h,i,c], accumulated in
+ * fp32 (o_lo may be NULL). */
+int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* o_lo,
+                            const void* d_o, float* delta, void* stream);
 
 /* Backward step 2: dK and dV.  Each kv head's gradient sums over the H/G query heads that
  * read it; the sum stays in registers (no atomics). */

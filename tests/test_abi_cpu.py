@@ -41,8 +41,8 @@ def test_status_strings():
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
 
 
-def _fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
-    return gqa.library().gqa_attn_fwd(ctypes.byref(p), q, k, v, o, lse, None)
+def _fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, o_lo=None):
+    return gqa.library().gqa_attn_fwd(ctypes.byref(p), q, k, v, o, o_lo, lse, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -76,6 +76,10 @@ def test_fwd_pointer_checks():
     assert _fwd(p, lse=None) == binding.GQA_ERR_INVALID_ARG
     assert _fwd(p, v=FAKE + 2) == binding.GQA_ERR_INVALID_ARG   # misaligned
     assert _fwd(p, o=FAKE + 8) == binding.GQA_ERR_INVALID_ARG
+    assert _fwd(p, o_lo=FAKE + 4) == binding.GQA_ERR_INVALID_ARG
+    # the rounding residual only exists for 16-bit outputs
+    p32 = gqa.make_problem(1, 4, 2, 128, dtype=binding.GQA_F32)
+    assert _fwd(p32, o_lo=FAKE) == binding.GQA_ERR_INVALID_ARG
 
 
 def test_empty_problem_is_a_noop():
@@ -90,16 +94,17 @@ def test_bwd_validation_and_workspace():
     p = gqa.make_problem(2, 8, 2, 100)
     need = lib.gqa_attn_bwd_workspace_bytes(ctypes.byref(p))
     assert need == ((2 * 8 * 100 * 4 + 255) // 256) * 256
-    args = [ctypes.byref(p)] + [FAKE] * 9
+    args = [ctypes.byref(p)] + [FAKE] * 4 + [None] + [FAKE] * 5   # o_lo = NULL
     assert lib.gqa_attn_bwd(*args, None, need, None) == binding.GQA_ERR_WORKSPACE
     assert lib.gqa_attn_bwd(*args, FAKE, need - 1, None) == binding.GQA_ERR_WORKSPACE
     bad = gqa.make_problem(2, 8, 3, 100)
-    assert lib.gqa_attn_bwd(ctypes.byref(bad), *([FAKE] * 9), FAKE, need, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd(ctypes.byref(bad), *([FAKE] * 10), FAKE, need, None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_dkdv(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) \
         == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_dq(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) \
         == binding.GQA_ERR_INVALID_ARG
-    assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, None, FAKE, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, None, None, FAKE, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE + 2, FAKE, FAKE, None) == binding.GQA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("S,causal,W,NS", [(1, True, 0, 0), (50, True, 0, 0), (50, False, 0, 0), (50, True, 7, 0),

@@ -10,6 +10,9 @@ full-size workloads on sampled rows (forward) or whole sampled kv groups
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -33,6 +36,11 @@ def _err(name, got, want, max_tol, mean_tol=None):
     err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
     mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
     print(f"  {name}: max {mx:.3e} mean {mean:.3e}", flush=True)
+    log = os.environ.get("GQA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "out": name,
+                                "max_abs": mx, "mean_abs": mean, "max_tol": max_tol, "mean_tol": mean_tol}) + "\n")
     assert np.isfinite(err).all(), f"{name}: non-finite values"
     assert mx <= max_tol, f"{name}: max abs error {mx:.3e} > {max_tol}"
     if mean_tol is not None:
@@ -47,25 +55,40 @@ def _kw(w: Workload):
     return dict(causal=w.causal, window=w.window, num_sinks=w.num_sinks)
 
 
-def run_fwd(w, q, k, v):
+def run_fwd(w, q, k, v, keep_residual=False):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    o, lse = gqa.gqa_attn_fwd(qd, kd, vd, scale=w.scale, **_kw(w))
+    res = gqa.gqa_attn_fwd(qd, kd, vd, scale=w.scale, keep_residual=keep_residual, **_kw(w))
     torch.cuda.synchronize()
-    return (qd, kd, vd), o, lse
+    if keep_residual:
+        return (qd, kd, vd), res[0], res[1], res[2]
+    return (qd, kd, vd), res[0], res[1]
 
 
 def check_full(w: Workload, with_bwd=True):
+    """Forward and backward in full.  16-bit inputs keep O's rounding residual for the
+    backward, as the autograd wrapper does."""
     print(f"[parity] {w}", flush=True)
     q, k, v, do = make_inputs(w, with_do=with_bwd)
-    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    lowp = w.dtype != "f32"
+    (qd, kd, vd), o, lse, *rest = run_fwd(w, q, k, v, keep_residual=lowp)
+    o_lo = rest[0] if rest else None
     O, L = ref.forward(q, k, v, scale=w.scale, **_kw(w))
     mx, mean, lmx = _tols(w)
     _err("O", _np(o), O, mx, mean)
     _err("lse", _np(lse), L, lmx)
     if not with_bwd:
         return
+    if o_lo is not None:
+        # the residual is what rounding O lost: at most half an ulp of the stored O
+        mant = 7 if w.dtype == "bf16" else 10
+        of = o.float()
+        _, e = torch.frexp(of)
+        half_ulp = torch.ldexp(torch.ones_like(of), (e - 1 - mant).to(torch.int32)) / 2
+        nz = of != 0
+        assert bool((o_lo.float().abs()[nz] <= half_ulp[nz]).all()), "o_lo exceeds half an ulp of O"
+        _err("O+o_lo", _np(o) + _np(o_lo), O, mx, mean)
     dod = do.cuda()
-    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, **_kw(w))
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, o_lo=o_lo, **_kw(w))
     torch.cuda.synchronize()
     dQ, dK, dV = ref.backward(q, k, v, do, scale=w.scale, **_kw(w))
     _err("dQ", _np(dq), dQ, mx, mean)
@@ -154,13 +177,15 @@ def test_c4_full_size_sampled_rows():
     _check_sampled_rows(w, sample_rows_c4(w), q, k, v, o, lse)
 
 
-def test_c5_full_size_bwd():
+@pytest.mark.parametrize("keep_residual", [False, True], ids=["plain", "residual"])
+def test_c5_full_size_bwd(keep_residual):
     w = WORKLOADS["c5"]
-    print(f"[parity] {w}", flush=True)
+    print(f"[parity] {w} residual={keep_residual}", flush=True)
     q, k, v, do = make_inputs(w)
-    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    (qd, kd, vd), o, lse, *rest = run_fwd(w, q, k, v, keep_residual=keep_residual)
     dod = do.cuda()
-    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, **_kw(w))
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, o_lo=rest[0] if rest else None,
+                                  **_kw(w))
     torch.cuda.synchronize()
     mx, mean, _ = _tols(w)
     hpg = w.H // w.G

@@ -62,13 +62,13 @@ def library() -> ctypes.CDLL:
     lib.gqa_visible_pairs.restype = ctypes.c_int64
     lib.gqa_visible_pairs.argtypes = [P]
     lib.gqa_attn_fwd.restype = ctypes.c_int
-    lib.gqa_attn_fwd.argtypes = [P, vp, vp, vp, vp, fp, vp]
+    lib.gqa_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, fp, vp]
     lib.gqa_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_attn_bwd_workspace_bytes.argtypes = [P]
     lib.gqa_attn_bwd.restype = ctypes.c_int
-    lib.gqa_attn_bwd.argtypes = [P, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.gqa_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
     lib.gqa_attn_bwd_preprocess.restype = ctypes.c_int
-    lib.gqa_attn_bwd_preprocess.argtypes = [P, vp, vp, fp, vp]
+    lib.gqa_attn_bwd_preprocess.argtypes = [P, vp, vp, vp, fp, vp]
     lib.gqa_attn_bwd_dkdv.restype = ctypes.c_int
     lib.gqa_attn_bwd_dkdv.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
     lib.gqa_attn_bwd_dq.restype = ctypes.c_int
@@ -143,8 +143,11 @@ def gqa_visible_pairs(S, causal=True, window=0, num_sinks=0) -> int:
 
 
 def gqa_attn_fwd(q, k, v, causal=True, window=0, num_sinks=0, scale=None, out=None, lse=None,
-                 stream=None):
-    """O [B,H,S,D] (q.dtype) and lse [B,H,S] (fp32) of causal grouped-query attention."""
+                 stream=None, o_lo=None, keep_residual=False):
+    """O [B,H,S,D] (q.dtype) and lse [B,H,S] (fp32) of causal grouped-query attention.
+
+    With ``keep_residual`` (or a given ``o_lo`` buffer) O's rounding residual is written
+    too and returned as a third value; pass it to the backward for a precise delta."""
     p = _problem_from(q, k, causal, window, num_sinks, scale)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, dtype=q.dtype, device=q.device)
@@ -155,9 +158,13 @@ def gqa_attn_fwd(q, k, v, causal=True, window=0, num_sinks=0, scale=None, out=No
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _need(out, "out", dtype=q.dtype, shape=q.shape, device=q.device)
     _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
-    _check(library().gqa_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                  _stream(stream)), "gqa_attn_fwd")
-    return out, lse
+    if keep_residual and o_lo is None:
+        o_lo = torch.empty_like(q)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
+    _check(library().gqa_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(o_lo),
+                                  _ptr(lse), _stream(stream)), "gqa_attn_fwd")
+    return (out, lse, o_lo) if o_lo is not None else (out, lse)
 
 
 def gqa_attn_bwd_workspace_bytes(q, k, causal=True, window=0, num_sinks=0, scale=None) -> int:
@@ -186,32 +193,36 @@ def _check_bwd_inputs(q, k, v, o, lse, d_o):
 
 
 def gqa_attn_bwd(q, k, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale=None, dq=None,
-                 dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV (fp32) of L = <O, dO>, from the forward's O and lse."""
+                 dk=None, dv=None, workspace=None, stream=None, o_lo=None):
+    """dQ, dK, dV (fp32) of L = <O, dO>, from the forward's O (and o_lo) and lse."""
     p = _problem_from(q, k, causal, window, num_sinks, scale)
     _check_bwd_inputs(q, k, v, o, lse, d_o)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
     dq, dk, dv = _grad_buffers(q, k, dq, dk, dv)
     nbytes = int(library().gqa_attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(library().gqa_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    _check(library().gqa_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse),
                                   _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
                                   _stream(stream)), "gqa_attn_bwd")
     return dq, dk, dv
 
 
-def gqa_attn_bwd_preprocess(o, d_o, delta=None, stream=None):
-    """delta [B,H,S] fp32 = rowsum(dO * O)."""
+def gqa_attn_bwd_preprocess(o, d_o, delta=None, stream=None, o_lo=None):
+    """delta [B,H,S] fp32 = rowsum(dO * (O + o_lo))."""
     _need(o, "o", device=o.device)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=o.dtype, shape=o.shape, device=o.device)
     _need(d_o, "d_o", dtype=o.dtype, shape=o.shape, device=o.device)
     B, H, S, D = o.shape
     if delta is None:
         delta = torch.empty((B, H, S), dtype=torch.float32, device=o.device)
     _need(delta, "delta", dtype=torch.float32, shape=(B, H, S), device=o.device)
     p = make_problem(B, H, 1, S, D, None, True, 0, 0, o.dtype)
-    _check(library().gqa_attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(d_o), _ptr(delta),
+    _check(library().gqa_attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(o_lo), _ptr(d_o), _ptr(delta),
                                              _stream(stream)), "gqa_attn_bwd_preprocess")
     return delta
 
@@ -246,17 +257,20 @@ class GqaAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal, window, num_sinks, scale):
-        o, lse = gqa_attn_fwd(q, k, v, causal, window, num_sinks, scale)
-        ctx.save_for_backward(q, k, v, o, lse)
+        res = gqa_attn_fwd(q, k, v, causal, window, num_sinks, scale, keep_residual=q.dtype != torch.float32)
+        o, lse = res[0], res[1]
+        o_lo = res[2] if len(res) > 2 else None
+        ctx.save_for_backward(q, k, v, o, lse, o_lo)
         ctx.cfg = (causal, window, num_sinks, scale)
+        ctx.mark_non_differentiable(lse)
         return o, lse
 
     @staticmethod
     def backward(ctx, d_o, d_lse):
-        q, k, v, o, lse = ctx.saved_tensors
+        q, k, v, o, lse, o_lo = ctx.saved_tensors
         causal, window, num_sinks, scale = ctx.cfg
         dq, dk, dv = gqa_attn_bwd(q, k, v, o, lse, d_o.contiguous().to(q.dtype), causal, window,
-                                  num_sinks, scale)
+                                  num_sinks, scale, o_lo=o_lo)
         return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
 
 

@@ -114,20 +114,22 @@ int64_t gqa_visible_pairs(const gqa_problem* p) {
   return pairs;
 }
 
-int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
-                 void* stream) {
+int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, void* o_lo,
+                 float* lse, void* stream) {
   int rc = check_problem(p);
   if (rc != GQA_OK) return rc;
   if (empty_problem(p)) return GQA_OK;
   if (!q || !k || !v || !o || !lse) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_lo))
     return GQA_ERR_INVALID_ARG;
+  if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
 
   FwdParams fp{};
   fp.q = q;
   fp.k = k;
   fp.v = v;
   fp.o = o;
+  fp.o_lo = o_lo;
   fp.lse = lse;
   fp.B = p->B;
   fp.H = p->H;
@@ -152,15 +154,18 @@ size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* d_o, float* delta, void* stream) {
+int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* o_lo, const void* d_o, float* delta,
+                            void* stream) {
   int rc = check_problem(p);
   if (rc != GQA_OK) return rc;
   if (empty_problem(p)) return GQA_OK;
   if (!o || !d_o || !delta) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(o) || !aligned16(d_o) || !aligned16(delta)) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(o_lo) || !aligned16(d_o) || !aligned16(delta)) return GQA_ERR_INVALID_ARG;
+  if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   bp.o = o;
+  bp.o_lo = o_lo;
   bp.d_o = d_o;
   bp.out_delta = delta;
   const long long rows = (long long)p->B * p->H * p->S;
@@ -216,8 +221,8 @@ int gqa_attn_bwd_dq(const gqa_problem* p, const void* q, const void* k, const vo
 }
 
 int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
-                 const float* lse, const void* d_o, float* dq, float* dk, float* dv, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 const void* o_lo, const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
   if (rc != GQA_OK) return rc;
   if (empty_problem(p)) return GQA_OK;
@@ -230,7 +235,7 @@ int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void*
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   float* delta = (float*)workspace;
-  if ((rc = gqa_attn_bwd_preprocess(p, o, d_o, delta, stream)) != GQA_OK) return rc;
+  if ((rc = gqa_attn_bwd_preprocess(p, o, o_lo, d_o, delta, stream)) != GQA_OK) return rc;
   if ((rc = gqa_attn_bwd_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, stream)) != GQA_OK) return rc;
   return gqa_attn_bwd_dq(p, q, k, v, lse, d_o, delta, dq, stream);
 }

@@ -25,7 +25,7 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // ------------------------------------------------------------------------------------
-// delta = rowsum(dO * O)
+// delta = rowsum(dO * O), with O = rounded O + its residual when the forward kept it
 // ------------------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
@@ -45,10 +45,13 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
     } else {
       const u32x4 a = *(const u32x4*)((const uint16_t*)p.o + off);
       const u32x4 b = *(const u32x4*)((const uint16_t*)p.d_o + off);
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (p.o_lo != nullptr) r = *(const u32x4*)((const uint16_t*)p.o_lo + off);
 #pragma unroll
       for (int w = 0; w < 4; ++w)
 #pragma unroll
-        for (int hi = 0; hi < 2; ++hi) acc += elem_to_f32<DT>(a[w], hi) * elem_to_f32<DT>(b[w], hi);
+        for (int hi = 0; hi < 2; ++hi)
+          acc += (elem_to_f32<DT>(a[w], hi) + elem_to_f32<DT>(r[w], hi)) * elem_to_f32<DT>(b[w], hi);
     }
   }
 #pragma unroll
@@ -92,6 +95,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int kw0 = K0 + wave * kTile;
   const int kw1 = imin(kw0 + kTile - 1, S - 1);
   const bool active = kw0 < S;
+  // Sink keys collect attention from every later query, so their dK and dV are sums of
+  // many large terms: there P and dS enter the MFMAs as a rounded value plus its rounded
+  // residual (two products each), which keeps the rounding of P and dS out of the sum.
+  const bool precise = m.window > 0 && kw0 < m.sinks;
 
   const uint16_t* kslab = (const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim;
   const uint16_t* vslab = (const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim;
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           }
         }
 
-        u32x4 pp[2][2], pds[2][2];  // [cb][t]
+        u32x4 pp[2][2], pds[2][2], pp_lo[2][2], pds_lo[2][2];  // [cb][t]
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -244,6 +251,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                               pack2<DT>(pv[6], pv[7])};
             pds[cb][t] = u32x4{pack2<DT>(dsv[0], dsv[1]), pack2<DT>(dsv[2], dsv[3]),
                                pack2<DT>(dsv[4], dsv[5]), pack2<DT>(dsv[6], dsv[7])};
+            if (precise) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                pp_lo[cb][t][w] = pack2_residual<DT>(pv[2 * w], pv[2 * w + 1], pp[cb][t][w]);
+                pds_lo[cb][t][w] = pack2_residual<DT>(dsv[2 * w], dsv[2 * w + 1], pds[cb][t][w]);
+              }
+            }
           }
 
 #pragma unroll
@@ -256,6 +270,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             for (int cb = 0; cb < 2; ++cb) {
               dv[db][cb] = mfma32<DT>(ado_t, pp[cb][t], dv[db][cb]);
               dk[db][cb] = mfma32<DT>(aq_t, pds[cb][t], dk[db][cb]);
+            }
+            if (precise) {
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb) {
+                dv[db][cb] = mfma32<DT>(ado_t, pp_lo[cb][t], dv[db][cb]);
+                dk[db][cb] = mfma32<DT>(aq_t, pds_lo[cb][t], dk[db][cb]);
+              }
             }
           }
       }

@@ -69,6 +69,23 @@ __device__ __forceinline__ uint32_t pack2<kDtF16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Residual of a rounded pair: pack2(a - round(a), b - round(b)), so that hi + lo carries
+// about twice the element type's mantissa (used where many products pile onto one sum).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_residual(float a, float b, uint32_t hi);
+
+template <>
+__device__ __forceinline__ uint32_t pack2_residual<kDtBF16>(float a, float b, uint32_t hi) {
+  const float ha = __builtin_bit_cast(float, hi << 16), hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+  return pack2<kDtBF16>(a - ha, b - hb);
+}
+
+template <>
+__device__ __forceinline__ uint32_t pack2_residual<kDtF16>(float a, float b, uint32_t hi) {
+  const f16x2 h = __builtin_bit_cast(f16x2, hi);
+  return pack2<kDtF16>(a - (float)h[0], b - (float)h[1]);
+}
+
 // 16-bit element (low half of w if hi == 0) to float.
 template <int DT>
 __device__ __forceinline__ float elem_to_f32(uint32_t w, int hi);

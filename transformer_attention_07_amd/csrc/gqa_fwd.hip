@@ -202,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
 
   if (!active) return;
   uint16_t* oslab = (uint16_t*)p.o + (size_t)(b * p.H + h) * S * kHeadDim;
+  uint16_t* olo_slab = p.o_lo ? (uint16_t*)p.o_lo + (size_t)(b * p.H + h) * S * kHeadDim : nullptr;
   float* lse_row = p.lse + (size_t)(b * p.H + h) * S;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -214,11 +215,16 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = db * 32 + 8 * r4 + 4 * hl;
-        const u32x2 w = {pack2<DT>(o[db][cb][4 * r4 + 0] * inv, o[db][cb][4 * r4 + 1] * inv),
-                         pack2<DT>(o[db][cb][4 * r4 + 2] * inv, o[db][cb][4 * r4 + 3] * inv)};
+        const float x0 = o[db][cb][4 * r4 + 0] * inv, x1 = o[db][cb][4 * r4 + 1] * inv;
+        const float x2 = o[db][cb][4 * r4 + 2] * inv, x3 = o[db][cb][4 * r4 + 3] * inv;
+        const u32x2 w = {pack2<DT>(x0, x1), pack2<DT>(x2, x3)};
         *(u32x2*)(oslab + (size_t)i * kHeadDim + d0) = w;
+        if (olo_slab != nullptr) {
+          const u32x2 r = {pack2_residual<DT>(x0, x1, w[0]), pack2_residual<DT>(x2, x3, w[1])};
+          *(u32x2*)(olo_slab + (size_t)i * kHeadDim + d0) = r;
+        }
       }
-    if (hl == 0) lse_row[i] = (mrow[cb] + __log2f(l)) * kLn2;
+    if (hl == 0) lse_row[i] = (mrow[cb] + log2f(l)) * kLn2;
   }
 }
 

@@ -123,6 +123,7 @@ struct FwdParams {
   const void* k;
   const void* v;
   void* o;
+  void* o_lo;        // optional: O minus its rounded value, in the element type
   float* lse;
   int B, H, G, S;
   float scale;       // softmax scale
@@ -138,6 +139,7 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* o;
+  const void* o_lo;  // optional rounding residual of O (preprocess only)
   const void* d_o;
   const float* lse;
   const float* delta;
