@@ -6,10 +6,13 @@
 // column (l % 32) and register r holds row 8*(r/4) + 4*(l/32) + (r%4).
 //
 // Two LDS tile layouts, both for 64 x 64 tiles of 16-bit elements (8 KiB):
-//   * row-major ("RM"): element (row, c) at row*128 + 16*((c/8) ^ (row%8)) + 2*(c%8).
-//     The 16-byte chunk is XOR-swizzled by the row so that 32 lanes reading the same
-//     chunk of 32 consecutive rows spread over all banks.  An A operand whose
-//     contraction index is the column (e.g. K for K Q^T) is one ds_read_b128 per lane.
+//   * row-major ("RM"): element (row, c) at row*128 + 16*((c/8) ^ swz(row)) + 2*(c%8),
+//     swz(row) = (row ^ (row >> 3)) & 7.  A 128-byte row covers half of the 64 banks;
+//     with this swizzle the 16 lanes of one LDS cycle reading the same chunk of 16
+//     consecutive rows hit 16 distinct 16-byte bank groups, and a transposed read
+//     (ds_read_b64_tr_b16: 4 consecutive rows x 32 bytes per 16 lanes) is conflict free.
+//     An A operand whose contraction index is the column (e.g. K for K Q^T) is one
+//     ds_read_b128 per lane.
 //   * transposed ("TR"): element (row, c) stored in LDS row c, so that an A operand
 //     whose contraction index is the tile row (e.g. V^T for V^T P^T) is contiguous.
 //     Within each group of 16 tile rows, row 8a + 4h + x (a, h in {0,1}, x in 0..3) is
@@ -17,7 +20,7 @@
 //     k-group h reads for contraction step t of key block kb are exactly the tile rows
 //     held by accumulator registers 8t..8t+7 of a lane of the same k-group, so an
 //     accumulator (S^T, P^T, dS) feeds the next MFMA as a B operand straight from
-//     registers.  Chunks are swizzled by (c % 8) as in RM.
+//     registers.  Chunks are swizzled by swz(c) as in RM.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -103,6 +106,25 @@ __device__ __forceinline__ float elem_to_f32<kDtF16>(uint32_t w, int hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// NaN-propagating maximum: lowers to v_maximum3_f32 with no canonicalising moves.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// acc + a.lo + a.hi for a packed pair of 16-bit values (v_dot2 with (1, 1)).
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t a, float acc);
+
+template <>
+__device__ __forceinline__ float add_pair<kDtBF16>(uint32_t a, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), ones, acc, false);
+}
+
+template <>
+__device__ __forceinline__ float add_pair<kDtF16>(uint32_t a, float acc) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), ones, acc, false);
+}
+
 // Value the lane (l ^ 32) holds, combined with ours: returns {ours, theirs} reduced by op.
 __device__ __forceinline__ float max_across_halves(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -119,10 +141,12 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 // ---- LDS layouts (byte offsets inside one 8 KiB tile) ----
-__device__ __forceinline__ int rm_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ int rm_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 // TR layout: byte offset of the 16-byte chunk `chunk` (0..7) of LDS row `c`.
-__device__ __forceinline__ int tr_chunk_off(int c, int chunk) { return c * 128 + ((chunk ^ (c & 7)) << 4); }
+__device__ __forceinline__ int tr_chunk_off(int c, int chunk) { return c * 128 + ((chunk ^ swz(c)) << 4); }
 
 // A-operand reads.  RM: rows blk*32 + (l%32), contraction chunk 2*ks + (l/32).
 __device__ __forceinline__ u32x4 lds_rm_operand(const char* tile, int blk, int ks, int l32, int hl) {
@@ -133,6 +157,27 @@ __device__ __forceinline__ u32x4 lds_rm_operand(const char* tile, int blk, int k
 __device__ __forceinline__ u32x4 lds_tr_operand(const char* tile, int blk, int kb, int t, int l32, int hl) {
   const int c = blk * 32 + l32;
   return *(const u32x4*)(tile + tr_chunk_off(c, kb * 4 + t * 2 + hl));
+}
+
+// Transposed A operand from a row-major tile with ds_read_b64_tr_b16.  Within each group of
+// 16 lanes that instruction returns to lane i element (i & 3) of the 4-element row that lane
+// 4e + (i >> 2) addressed, for e = 0..3.  If lane j of the group addresses row r0 + (j >> 2),
+// columns c0 + 4 (j & 3) .. + 3, lane i therefore receives rows r0 .. r0 + 3 of column c0 + i:
+// a column segment, which is what an operand contracting over tile rows needs.
+// Output: the A operand for output rows (tile columns) blk*32 + (l%32) and contraction rows
+// 32*kb + 16*t + {4h..4h+3, 8+4h..8+4h+3} (h = l/32), the order of the TR layout above.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_rm_transposed_operand(const char* tile, int blk, int kb, int t, int lane) {
+  const int h = lane >> 5;
+  const int c0 = blk * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int r0 = kb * 32 + 16 * t + 4 * h + ((lane & 15) >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char* pa = tile + rm_off(r0, c0 >> 3) + (c0 & 7) * 2;
+  const char* pb = tile + rm_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)pa);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)pb);
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
 // ---- staging of a 64 x 64 tile from global memory ----
@@ -178,6 +223,34 @@ __device__ __forceinline__ void unit_store_tr(char* tile, const Unit& u, int r0,
     }
     *(u32x2*)(tile + tr_chunk_off(c, chunk) + a * 8) = u32x2{lo, hi};
   }
+}
+
+// ---- buffer loads ----
+// A buffer resource over a [rows][64] slab of 16-bit elements: raw loads at or past the end
+// of the slab return zero, so ragged tiles need no bounds branches.  Offsets are bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int rows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, rows * kHeadDim * 2, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void unit_load_buf(Unit& u, __amdgpu_buffer_rsrc_t r, int row0, int dc) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) u.x[n] = buf_load16(r, (row0 + n) * (kHeadDim * 2) + dc * 16);
+}
+
+// Row-major-only staging: register n holds row row0 + (n ^ flip), flip = 1 for odd units, so
+// that one store instruction writes rows of both parities (both halves of the banks).
+__device__ __forceinline__ void unit_load_buf_rm(Unit& u, __amdgpu_buffer_rsrc_t r, int row0, int dc, int flip) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) u.x[n] = buf_load16(r, (row0 + (n ^ flip)) * (kHeadDim * 2) + dc * 16);
+}
+
+__device__ __forceinline__ void unit_store_rm_flip(char* tile, const Unit& u, int r0, int dc, int flip) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) *(u32x4*)(tile + rm_off(r0 + (n ^ flip), dc)) = u.x[n];
 }
 
 // Row of the accumulator register r of this lane, inside a 32-row block.
