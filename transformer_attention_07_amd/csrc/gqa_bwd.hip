@@ -2,13 +2,17 @@
 // inputs, fp32 gradients).  Loss convention L = <O, dO>.
 //
 //   preprocess : delta_i = sum_c dO_ic O_ic                       (HBM-bound, fp32)
-//   dK/dV      : per (b, g, 256-key block), 4 waves x 64 keys.  For every query head of
-//                the group and every query tile that sees the block:
+//   dK/dV      : per (b, g, 256-key block), 8 waves x 32 keys (two waves per SIMD).  For
+//                every query head of the group and every query tile that sees the block:
 //                  S  = Q K^T        P = exp(scale*S - lse)   (recomputed from the saved lse)
-//                  dP = dO V^T       dS = P * (dP - delta)
+//                  dP - delta = dO V^T + (-delta)  (the accumulator starts at -delta)
+//                  dS = P * (dP - delta)
 //                  dV^T += dO^T P    dK^T += Q^T dS           (scale applied at the end)
 //                The sum over the H/G heads of the group stays in registers: no atomics.
-//   dQ         : per (b, h, 64-row tile), the forward's decomposition.  For every key
+//                Q and dO tiles are staged row-major; the transposed operands dO^T and Q^T
+//                come from the same tiles through ds_read_b64_tr_b16.
+//   dQ         : per (b, h, 64-row tile), the forward's decomposition (two waves per
+//                SIMD).  For every key
 //                tile it sees: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
 //                dQ^T += K^T dS^T.  Deterministic (each dQ element has one writer).
 //
@@ -63,25 +67,105 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 // dK, dV
 // ------------------------------------------------------------------------------------
 struct DkdvStage {
-  char q_rm[8192];
-  char q_tr[8192];
-  char do_rm[8192];
-  char do_tr[8192];
-  float lse2[64];
-  float delta[64];
+  char q_rm[8192];   // Q tile, row-major (rows = queries)
+  char do_rm[8192];  // dO tile, row-major
+  float lse2[64];    // lse * log2(e); +inf past the end of the sequence (P = 0 there)
+  float ndelta[64];  // -delta; 0 past the end
 };
 
+// Per-wave state of the dK/dV pass: 32 keys (one column block) of one kv head.
 template <int DT>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) DkdvStage stage[2];
+struct DkdvWave {
+  int lane, l32, hl;
+  int kw0, kw1;
+  MaskSpec m;
+  float c2;
+  u32x4 kf[4], vf[4];  // K and V rows as B operands [contraction step]
+  f32x16 dk[2], dv[2];  // transposed accumulators [d block]
 
+  // one 32-query block qb of the staged tile (rows qr0 ..): both products for dK and dV
+  template <bool PRECISE>
+  __device__ __forceinline__ void block(const DkdvStage& sb, int qb, int qr0, bool partial) {
+    f32x16 s, dp;
+    f32x16 nd;  // -delta of this lane's 16 rows: the initial dP accumulator, so dP' = dP - delta
+    float L[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 lv = *(const f32x4*)(sb.lse2 + qb * 32 + 8 * r4 + 4 * hl);
+      const f32x4 dv4 = *(const f32x4*)(sb.ndelta + qb * 32 + 8 * r4 + 4 * hl);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        L[4 * r4 + x] = lv[x];
+        nd[4 * r4 + x] = dv4[x];
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 aq = lds_rm_operand(sb.q_rm, qb, ks, l32, hl);
+      const u32x4 ado = lds_rm_operand(sb.do_rm, qb, ks, l32, hl);
+      s = mfma32<DT>(aq, kf[ks], ks == 0 ? f32x16{} : s);
+      dp = mfma32<DT>(ado, vf[ks], ks == 0 ? nd : dp);
+    }
+    if (__builtin_expect(partial, 0)) {
+      // lane = key column j, register r = query row qr0 + 4*hl + rr(r)
+      const int j = kw0 + l32;
+      const int base = qr0 + 4 * hl;
+      const int lo = m.causal ? j - base : -(1 << 30);                 // rr >= lo: i >= j
+      const bool sink = j < m.sinks;
+      const int whi = m.window > 0 ? j + m.window - base : (1 << 30);  // rr < whi: in window
+      const bool key_ok = j < m.S;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 8 * (r >> 2) + (r & 3);
+        const bool ok = key_ok && rr >= lo && (sink || rr < whi);
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+    u32x4 pp[2], pds[2], pp_lo[2], pds_lo[2];  // [t]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t + e;
+        pv[e] = exp2_fast(__builtin_fmaf(s[r], c2, -L[r]));
+        dsv[e] = pv[e] * dp[r];
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pp[t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
+        pds[t][w] = pack2<DT>(dsv[2 * w], dsv[2 * w + 1]);
+        if (PRECISE) {
+          pp_lo[t][w] = pack2_residual<DT>(pv[2 * w], pv[2 * w + 1], pp[t][w]);
+          pds_lo[t][w] = pack2_residual<DT>(dsv[2 * w], dsv[2 * w + 1], pds[t][w]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const u32x4 ado_t = lds_rm_transposed_operand(sb.do_rm, db, qb, t, lane);
+        const u32x4 aq_t = lds_rm_transposed_operand(sb.q_rm, db, qb, t, lane);
+        dv[db] = mfma32<DT>(ado_t, pp[t], dv[db]);
+        dk[db] = mfma32<DT>(aq_t, pds[t], dk[db]);
+        if (PRECISE) {
+          dv[db] = mfma32<DT>(ado_t, pp_lo[t], dv[db]);
+          dk[db] = mfma32<DT>(aq_t, pds_lo[t], dk[db]);
+        }
+      }
+  }
+};
+
+// The whole dK/dV pass for one workgroup.  Kept out of line so that the rare variant for
+// key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
+// allocation instead of raising the common variant's.
+template <int DT, bool PRECISE>
+__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& p, DkdvStage* stage) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
   const int S = p.S;
-  const MaskSpec m = p.mask;
   const int hpg = p.H / p.G;
 
   // heaviest (earliest) key blocks first
@@ -92,85 +176,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int g = rest % p.G;
   const int K0 = kblk * 4 * kTile;
   const int K1 = imin(K0 + 4 * kTile, S) - 1;
-  const int kw0 = K0 + wave * kTile;
-  const int kw1 = imin(kw0 + kTile - 1, S - 1);
-  const bool active = kw0 < S;
-  // Sink keys collect attention from every later query, so their dK and dV are sums of
-  // many large terms: there P and dS enter the MFMAs as a rounded value plus its rounded
-  // residual (two products each), which keeps the rounding of P and dS out of the sum.
-  const bool precise = m.window > 0 && kw0 < m.sinks;
 
-  const uint16_t* kslab = (const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim;
-  const uint16_t* vslab = (const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim;
+  DkdvWave<DT> W;
+  W.lane = lane;
+  W.l32 = lane & 31;
+  W.hl = lane >> 5;
+  W.kw0 = K0 + wave * 32;
+  W.kw1 = imin(W.kw0 + 31, S - 1);
+  W.m = p.mask;
+  W.c2 = p.scale_log2;
+  const bool active = W.kw0 < S;
 
-  // K and V rows of this wave as B operands: column block cb (keys kw0 + 32cb + l32)
-  u32x4 kf[2][4], vf[2][4];
+  const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim, S);
+  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim, S);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int row = kw0 + cb * 32 + l32;
+  for (int ks = 0; ks < 4; ++ks) {
+    const int off = (W.kw0 + W.l32) * 128 + ks * 32 + W.hl * 16;
+    W.kf[ks] = buf_load16(krs, off);
+    W.vf[ks] = buf_load16(vrs, off);
+  }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (active && row < S) {
-        kf[cb][ks] = *(const u32x4*)(kslab + (size_t)row * kHeadDim + ks * 16 + hl * 8);
-        vf[cb][ks] = *(const u32x4*)(vslab + (size_t)row * kHeadDim + ks * 16 + hl * 8);
-      } else {
-        kf[cb][ks] = u32x4{0u, 0u, 0u, 0u};
-        vf[cb][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  for (int db = 0; db < 2; ++db) {
+    W.dk[db] = f32x16{};
+    W.dv[db] = f32x16{};
   }
 
-  f32x16 dk[2][2], dv[2][2];  // transposed accumulators [d block][key column block]
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      dk[db][cb] = f32x16{};
-      dv[db][cb] = f32x16{};
-    }
-
-  // staging roles: threads 0..127 stage Q units, 128..255 dO units (both RM and TR);
-  // threads 0..63 also stage lse (in log2 units), 64..127 delta.
-  const int kind = tid >> 7;
+  // staging roles: threads 0..127 stage Q tiles, 128..255 dO tiles (row-major);
+  // threads 256..319 stage lse (log2 units), 320..383 -delta.
+  const int kind = wave >> 1;  // 0: Q, 1: dO, 2..3: statistics
   const int unit = tid & 127;
   const int ur0 = (unit >> 3) * 4;
   const int udc = unit & 7;
+  const int flip = (unit >> 3) & 1;
   Unit st;
   float st_f = 0.f;
 
-  const TileRanges tr = query_tiles_for_keys(m, K0, K1);
+  const TileRanges tr = query_tiles_for_keys(W.m, K0, K1);
   const int nq = tr.count();
   const int n_iter = nq * hpg;
-  const float c2 = p.scale_log2;
-
-  auto load_stage = [&](int iter) {
+  auto load_stage = [&](int iter) __attribute__((always_inline)) {
     const int hh = iter / nq;
     const int qt = tr.tile(iter % nq);
-    const int h = g * hpg + hh;
-    const size_t slab = (size_t)(b * p.H + h) * S;
-    const uint16_t* src = (const uint16_t*)(kind == 0 ? p.q : p.d_o) + slab * kHeadDim;
-    unit_load(st, src, qt * kTile + ur0, udc, S);
-    if (tid < 128) {
+    const size_t slab = (size_t)(b * p.H + g * hpg + hh) * S;
+    if (kind < 2) {
+      const __amdgpu_buffer_rsrc_t r =
+          slab_rsrc((const uint16_t*)(kind == 0 ? p.q : p.d_o) + slab * kHeadDim, S);
+      unit_load_buf_rm(st, r, qt * kTile + ur0, udc, flip);
+    } else if (tid < 384) {
       const int i = qt * kTile + (tid & 63);
-      if (tid < 64)
+      if (tid < 320)
         st_f = (i < S) ? p.lse[slab + i] * kLog2e : INFINITY;
       else
-        st_f = (i < S) ? p.delta[slab + i] : 0.f;
+        st_f = (i < S) ? -p.delta[slab + i] : 0.f;
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf) __attribute__((always_inline)) {
     DkdvStage& sb = stage[buf];
-    if (kind == 0) {
-      unit_store_rm(sb.q_rm, st, ur0, udc);
-      unit_store_tr(sb.q_tr, st, ur0, udc);
-    } else {
-      unit_store_rm(sb.do_rm, st, ur0, udc);
-      unit_store_tr(sb.do_tr, st, ur0, udc);
-    }
-    if (tid < 64)
-      sb.lse2[tid] = st_f;
-    else if (tid < 128)
-      sb.delta[tid - 64] = st_f;
+    if (kind < 2)
+      unit_store_rm_flip(kind == 0 ? sb.q_rm : sb.do_rm, st, ur0, udc, flip);
+    else if (tid < 320)
+      sb.lse2[tid - 256] = st_f;
+    else if (tid < 384)
+      sb.ndelta[tid - 320] = st_f;
   };
 
   if (n_iter > 0) {
@@ -184,104 +251,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const bool more = it + 1 < n_iter;
     if (more) load_stage(it + 1);
     const DkdvStage& sb = stage[it & 1];
-
     if (active) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qr0 = qt * kTile + qb * 32;
-        if (qr0 >= S) continue;
-        const int cls = classify(m, qr0, imin(qr0 + 31, S - 1), kw0, kw1);
+        const int cls = qr0 < S ? classify(W.m, qr0, imin(qr0 + 31, S - 1), W.kw0, W.kw1) : (int)kEmpty;
         if (cls == kEmpty) continue;
-
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          s[cb] = f32x16{};
-          dp[cb] = f32x16{};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 aq = lds_rm_operand(sb.q_rm, qb, ks, l32, hl);
-          const u32x4 ado = lds_rm_operand(sb.do_rm, qb, ks, l32, hl);
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            s[cb] = mfma32<DT>(aq, kf[cb][ks], s[cb]);
-            dp[cb] = mfma32<DT>(ado, vf[cb][ks], dp[cb]);
-          }
-        }
-
-        // per-row statistics of the 16 rows this lane's registers hold
-        float L[16], Dl[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 lv = *(const f32x4*)(sb.lse2 + qb * 32 + 8 * r4 + 4 * hl);
-          const f32x4 dv4 = *(const f32x4*)(sb.delta + qb * 32 + 8 * r4 + 4 * hl);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            L[4 * r4 + x] = lv[x];
-            Dl[4 * r4 + x] = dv4[x];
-          }
-        }
-
-        if (cls == kPartial) {
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const int j = kw0 + cb * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = qr0 + acc_row(r, hl);
-              if (!visible(m, i, j)) s[cb][r] = -INFINITY;
-            }
-          }
-        }
-
-        u32x4 pp[2][2], pds[2][2], pp_lo[2][2], pds_lo[2][2];  // [cb][t]
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            float pv[8], dsv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * t + e;
-              pv[e] = exp2_fast(__builtin_fmaf(s[cb][r], c2, -L[r]));
-              dsv[e] = pv[e] * (dp[cb][r] - Dl[r]);
-            }
-            pp[cb][t] = u32x4{pack2<DT>(pv[0], pv[1]), pack2<DT>(pv[2], pv[3]), pack2<DT>(pv[4], pv[5]),
-                              pack2<DT>(pv[6], pv[7])};
-            pds[cb][t] = u32x4{pack2<DT>(dsv[0], dsv[1]), pack2<DT>(dsv[2], dsv[3]),
-                               pack2<DT>(dsv[4], dsv[5]), pack2<DT>(dsv[6], dsv[7])};
-            if (precise) {
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                pp_lo[cb][t][w] = pack2_residual<DT>(pv[2 * w], pv[2 * w + 1], pp[cb][t][w]);
-                pds_lo[cb][t][w] = pack2_residual<DT>(dsv[2 * w], dsv[2 * w + 1], pds[cb][t][w]);
-              }
-            }
-          }
-
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const u32x4 ado_t = lds_tr_operand(sb.do_tr, db, qb, t, l32, hl);
-            const u32x4 aq_t = lds_tr_operand(sb.q_tr, db, qb, t, l32, hl);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              dv[db][cb] = mfma32<DT>(ado_t, pp[cb][t], dv[db][cb]);
-              dk[db][cb] = mfma32<DT>(aq_t, pds[cb][t], dk[db][cb]);
-            }
-            if (precise) {
-#pragma unroll
-              for (int cb = 0; cb < 2; ++cb) {
-                dv[db][cb] = mfma32<DT>(ado_t, pp_lo[cb][t], dv[db][cb]);
-                dk[db][cb] = mfma32<DT>(aq_t, pds_lo[cb][t], dk[db][cb]);
-              }
-            }
-          }
+        W.template block<PRECISE>(sb, qb, qr0, cls != kFull);
       }
     }
-
     if (more) store_stage((it + 1) & 1);
     __syncthreads();
   }
@@ -289,40 +267,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   if (!active) return;
   float* dkslab = p.dk + (size_t)(b * p.G + g) * S * kHeadDim;
   float* dvslab = p.dv + (size_t)(b * p.G + g) * S * kHeadDim;
+  const int j = W.kw0 + W.l32;
+  if (j >= S) return;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int j = kw0 + cb * 32 + l32;
-    if (j >= S) continue;
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * hl;
-        const f32x4 kv = {dk[db][cb][4 * r4] * p.scale, dk[db][cb][4 * r4 + 1] * p.scale,
-                          dk[db][cb][4 * r4 + 2] * p.scale, dk[db][cb][4 * r4 + 3] * p.scale};
-        const f32x4 vv = {dv[db][cb][4 * r4], dv[db][cb][4 * r4 + 1], dv[db][cb][4 * r4 + 2],
-                          dv[db][cb][4 * r4 + 3]};
-        *(f32x4*)(dkslab + (size_t)j * kHeadDim + d0) = kv;
-        *(f32x4*)(dvslab + (size_t)j * kHeadDim + d0) = vv;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * W.hl;
+      const f32x4 kv = {W.dk[db][4 * r4] * p.scale, W.dk[db][4 * r4 + 1] * p.scale, W.dk[db][4 * r4 + 2] * p.scale,
+                        W.dk[db][4 * r4 + 3] * p.scale};
+      const f32x4 vv = {W.dv[db][4 * r4], W.dv[db][4 * r4 + 1], W.dv[db][4 * r4 + 2], W.dv[db][4 * r4 + 3]};
+      *(f32x4*)(dkslab + (size_t)j * kHeadDim + d0) = kv;
+      *(f32x4*)(dvslab + (size_t)j * kHeadDim + d0) = vv;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) DkdvStage stage[2];
+  // Sink keys collect attention from every later query, so their dK and dV are sums of
+  // many large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value
+  // plus its rounded residual (two products each), which keeps their rounding out of the sum.
+  const int kblk = (int)(blockIdx.x / (p.B * p.G));
+  if (p.mask.window > 0 && kblk * 4 * kTile < p.mask.sinks)
+    dkdv_block<DT, true>(p, stage);
+  else
+    dkdv_block<DT, false>(p, stage);
 }
 
 // ------------------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------------------
-struct DqStage {
-  char k_rm[8192];
-  char k_tr[8192];
-  char v_rm[8192];
-};
-
 template <int DT>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) DqStage stage[2];
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char k_lds[2][8192];  // row-major K tiles
+  __shared__ __attribute__((aligned(16))) char v_lds[2][8192];  // row-major V tiles
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
@@ -343,10 +325,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const bool active = q0 < S;
 
   const size_t qslab_rows = (size_t)(b * p.H + h) * S;
-  const uint16_t* qslab = (const uint16_t*)p.q + qslab_rows * kHeadDim;
-  const uint16_t* doslab = (const uint16_t*)p.d_o + qslab_rows * kHeadDim;
-  const uint16_t* kslab = (const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim;
-  const uint16_t* vslab = (const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim;
+  const __amdgpu_buffer_rsrc_t qrs = slab_rsrc((const uint16_t*)p.q + qslab_rows * kHeadDim, S);
+  const __amdgpu_buffer_rsrc_t dors = slab_rsrc((const uint16_t*)p.d_o + qslab_rows * kHeadDim, S);
+  const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim, S);
+  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim, S);
 
   u32x4 qf[2][4], df[2][4];
   float lse2[2], dlt[2];
@@ -356,13 +338,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     const bool ok = active && row < S;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ok) {
-        qf[cb][ks] = *(const u32x4*)(qslab + (size_t)row * kHeadDim + ks * 16 + hl * 8);
-        df[cb][ks] = *(const u32x4*)(doslab + (size_t)row * kHeadDim + ks * 16 + hl * 8);
-      } else {
-        qf[cb][ks] = u32x4{0u, 0u, 0u, 0u};
-        df[cb][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int off = row * 128 + ks * 32 + hl * 16;
+      qf[cb][ks] = buf_load16(qrs, off);
+      df[cb][ks] = buf_load16(dors, off);
     }
     lse2[cb] = ok ? p.lse[qslab_rows + row] * kLog2e : INFINITY;
     dlt[cb] = ok ? p.delta[qslab_rows + row] : 0.f;
@@ -374,77 +352,64 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) dq[db][cb] = f32x16{};
 
-  // staging roles: threads 0..127 stage K (RM and TR), 128..255 stage V (RM)
-  const int kind = tid >> 7;
+  // staging roles: threads 0..127 stage K tiles, 128..255 V tiles (row-major)
+  const int kind = wave >> 1;
   const int unit = tid & 127;
   const int ur0 = (unit >> 3) * 4;
   const int udc = unit & 7;
-  const uint16_t* stage_slab = kind == 0 ? kslab : vslab;
+  const int flip = (unit >> 3) & 1;
   Unit st;
 
   const TileRanges tr = key_tiles_for_rows(m, Q0, Q1);
   const int nt = tr.count();
   const float c2 = p.scale_log2;
+  auto tile_row = [&](int n) __attribute__((always_inline)) { return n < nt ? tr.tile(n) * kTile : S; };
 
-  auto store_stage = [&](int buf) {
-    if (kind == 0) {
-      unit_store_rm(stage[buf].k_rm, st, ur0, udc);
-      unit_store_tr(stage[buf].k_tr, st, ur0, udc);
-    } else {
-      unit_store_rm(stage[buf].v_rm, st, ur0, udc);
-    }
-  };
-
-  if (nt > 0) {
-    unit_load(st, stage_slab, tr.tile(0) * kTile + ur0, udc, S);
-    store_stage(0);
-  }
+  unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(0) + ur0, udc, flip);
+  unit_store_rm_flip(kind == 0 ? k_lds[0] : v_lds[0], st, ur0, udc, flip);
   __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
-    const int kt = tr.tile(it);
-    const int k0 = kt * kTile;
-    const bool more = it + 1 < nt;
-    if (more) unit_load(st, stage_slab, tr.tile(it + 1) * kTile + ur0, udc, S);
-    const DqStage& sb = stage[it & 1];
-
+    const int k0 = tr.tile(it) * kTile;
+    unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(it + 1) + ur0, udc, flip);
+    const char* kl = k_lds[it & 1];
+    const char* vl = v_lds[it & 1];
     if (active) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int kr0 = k0 + kb * 32;
-        if (kr0 >= S) continue;
-        const int cls = classify(m, q0, q1, kr0, kr0 + 31);
+        const int cls = kr0 < S ? classify(m, q0, q1, kr0, kr0 + 31) : (int)kEmpty;
         if (cls == kEmpty) continue;
-
         f32x16 s[2], dp[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          s[cb] = f32x16{};
-          dp[cb] = f32x16{};
-        }
-#pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 ak = lds_rm_operand(sb.k_rm, kb, ks, l32, hl);
-          const u32x4 av = lds_rm_operand(sb.v_rm, kb, ks, l32, hl);
+          const u32x4 ak = lds_rm_operand(kl, kb, ks, l32, hl);
+          const u32x4 av = lds_rm_operand(vl, kb, ks, l32, hl);
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
-            s[cb] = mfma32<DT>(ak, qf[cb][ks], s[cb]);
-            dp[cb] = mfma32<DT>(av, df[cb][ks], dp[cb]);
+            s[cb] = mfma32<DT>(ak, qf[cb][ks], ks == 0 ? f32x16{} : s[cb]);
+            dp[cb] = mfma32<DT>(av, df[cb][ks], ks == 0 ? f32x16{} : dp[cb]);
           }
         }
-
-        if (cls == kPartial) {
+        if (__builtin_expect(cls != kFull, 0)) {
+          // lane = query column i, register r = key kr0 + 4*hl + rr(r)
+          const int base = kr0 + 4 * hl;
+          const int kmax = m.S - 1 - base;
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             const int i = q0 + cb * 32 + l32;
+            const int causal_hi = m.causal ? i - base : kmax;
+            const int hi = causal_hi < kmax ? causal_hi : kmax;
+            const int win_lo = m.window > 0 ? i - m.window + 1 - base : -(1 << 30);
+            const int sink_hi = m.sinks - 1 - base;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int j = kr0 + acc_row(r, hl);
-              if (!visible(m, i, j)) s[cb][r] = -INFINITY;
+              const int rr = 8 * (r >> 2) + (r & 3);
+              const bool ok = (rr <= hi) && (rr >= win_lo || rr <= sink_hi);
+              s[cb][r] = ok ? s[cb][r] : -INFINITY;
             }
           }
         }
-
         u32x4 pds[2][2];  // [cb][t]
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -457,22 +422,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
               const float pv = exp2_fast(__builtin_fmaf(s[cb][r], c2, -lse2[cb]));
               dsv[e] = pv * (dp[cb][r] - dlt[cb]);
             }
-            pds[cb][t] = u32x4{pack2<DT>(dsv[0], dsv[1]), pack2<DT>(dsv[2], dsv[3]),
-                               pack2<DT>(dsv[4], dsv[5]), pack2<DT>(dsv[6], dsv[7])};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pds[cb][t][w] = pack2<DT>(dsv[2 * w], dsv[2 * w + 1]);
           }
-
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const u32x4 akt = lds_tr_operand(sb.k_tr, db, kb, t, l32, hl);
+          for (int db = 0; db < 2; ++db) {
+            const u32x4 akt = lds_rm_transposed_operand(kl, db, kb, t, lane);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) dq[db][cb] = mfma32<DT>(akt, pds[cb][t], dq[db][cb]);
           }
       }
     }
-
-    if (more) store_stage((it + 1) & 1);
+    unit_store_rm_flip(kind == 0 ? k_lds[(it + 1) & 1] : v_lds[(it + 1) & 1], st, ur0, udc, flip);
     __syncthreads();
   }
 
@@ -489,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         const int d0 = db * 32 + 8 * r4 + 4 * hl;
         const f32x4 w = {dq[db][cb][4 * r4] * p.scale, dq[db][cb][4 * r4 + 1] * p.scale,
                          dq[db][cb][4 * r4 + 2] * p.scale, dq[db][cb][4 * r4 + 3] * p.scale};
-        *(f32x4*)(dqslab + (size_t)i * kHeadDim + d0) = w;
+        *(f32x4*)(p.dq + (qslab_rows + i) * kHeadDim + d0) = w;
       }
   }
 }
@@ -509,7 +472,7 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s) {
-  dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(256);
+  dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(512);
   void* args[] = {(void*)&p};
   if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtBF16>, grid, block, args, 0, s);
   return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtF16>, grid, block, args, 0, s);
