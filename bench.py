@@ -46,6 +46,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration runs)")
+    ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of --workload, then exit")
     return ap.parse_args()
 
 
@@ -82,6 +85,53 @@ def load_traffic(kernel, wname):
     if not ent or rec.get("source_digest") != source_digest():
         return None
     return ent.get("bytes_per_launch")
+
+
+KERNEL_KEYS = {"fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
+               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "copyBuffer": "copy"}
+COPY_BYTES = 1 << 30
+
+
+def reduce_counters(fetch_csv, write_csv, wname):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled so that the 1 GiB calibration copy reads as exactly 1 GiB in and 1 GiB out."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = next((v for k, v in KERNEL_KEYS.items() if k in r["Kernel_Name"]), None)
+                if key:
+                    acc.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / fetch["copy"], COPY_BYTES / write["copy"]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_digest") != source_digest():
+        rec = {"kernels": {}}
+    rec.update(source_digest=source_digest(),
+               note="HBM bytes per launch = FETCH_SIZE*fetch_scale + WRITE_SIZE*write_scale (counters in KiB); "
+                    "scales make a plain 1 GiB device copy read 1 GiB in and 1 GiB out")
+    rec.setdefault("calibration", {})[wname] = {"fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)}
+    for k in fetch:
+        if k == "copy" or k not in write:
+            continue
+        rec["kernels"][f"{k}@{wname}"] = {
+            "fetch_bytes": round(fetch[k] * f_scale), "write_bytes": round(write[k] * w_scale),
+            "bytes_per_launch": round(fetch[k] * f_scale + write[k] * w_scale)}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec["kernels"], indent=1))
 
 
 def cpu_baseline(w, inputs, budget_s):
@@ -128,6 +178,9 @@ def main():
         print("bench.py runs on exactly one GPU: the attention path is built and measured on a "
               "single MI355X (no collectives, no sharding); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.reduce_counters:
+        reduce_counters(*args.reduce_counters, workload(args.workload).name)
+        return
 
     import torch
 
