@@ -6,11 +6,16 @@
 // column (l % 32) and register r holds row 8*(r/4) + 4*(l/32) + (r%4).
 //
 // Two LDS tile layouts, both for 64 x 64 tiles of 16-bit elements (8 KiB):
-//   * row-major ("RM"): element (row, c) at row*128 + 16*((c/8) ^ swz(row)) + 2*(c%8),
-//     swz(row) = (row ^ (row >> 3)) & 7.  A 128-byte row covers half of the 64 banks;
-//     with this swizzle the 16 lanes of one LDS cycle reading the same chunk of 16
-//     consecutive rows hit 16 distinct 16-byte bank groups, and a transposed read
-//     (ds_read_b64_tr_b16: 4 consecutive rows x 32 bytes per 16 lanes) is conflict free.
+//   * row-major ("RM"): element (row, c) at row*128 + 16*((c/8) ^ swz(row)) + 2*(c%8).
+//     A 128-byte row covers half of the 64 banks, so bank group = (row parity, stored
+//     chunk).  swz maps row bits (r0, r1, r2, r3) to chunk-XOR bits
+//     (r2 ^ r3, r0 ^ r2, r1), which makes both read shapes conflict free:
+//       - ds_read_b128 of one chunk over 16 aligned consecutive rows (16 lanes per LDS
+//         cycle): for either parity the 8 rows take 8 distinct swz values;
+//       - ds_read_b64_tr_b16 over 4 aligned consecutive rows x 4 aligned chunks (32 lanes
+//         per cycle): rows r and r + 2 share a parity and differ in swz bit 2, so they land
+//         on the two disjoint aligned 4-chunk groups.
+//     Stores write 8 distinct chunks of one row and rows of both parities per cycle.
 //     An A operand whose contraction index is the column (e.g. K for K Q^T) is one
 //     ds_read_b128 per lane.
 //   * transposed ("TR"): element (row, c) stored in LDS row c, so that an A operand
@@ -141,7 +146,9 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 // ---- LDS layouts (byte offsets inside one 8 KiB tile) ----
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 2) ^ (row >> 3)) & 1) | (((row ^ (row >> 2)) & 1) << 1) | ((row & 2) << 1);
+}
 
 __device__ __forceinline__ int rm_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
