@@ -5,21 +5,29 @@
 //   dK/dV      : per (b, g, 256-key block), 8 waves x 32 keys (two waves per SIMD).  For
 //                every query head of the group and every query tile that sees the block:
 //                  S  = Q K^T        P = exp(scale*S - lse)   (recomputed from the saved lse)
-//                  dP - delta = dO V^T + (-delta)  (the accumulator starts at -delta)
-//                  dS = P * (dP - delta)
+//                  delta - dP = dO (-V)^T + delta  (V enters negated, the accumulator
+//                                                    starts at delta)
+//                  dS = P * (dP - delta) = -P * (delta - dP)
 //                  dV^T += dO^T P    dK^T += Q^T dS           (scale applied at the end)
 //                The sum over the H/G heads of the group stays in registers: no atomics.
-//                Q and dO tiles are staged row-major; the transposed operands dO^T and Q^T
-//                come from the same tiles through ds_read_b64_tr_b16.
+//                Q and dO tiles and the lse / delta rows arrive by direct loads into LDS
+//                (double-buffered, one barrier per tile); the transposed operands dO^T
+//                and Q^T come from the row-major tiles through ds_read_b64_tr_b16.
 //   dQ         : per (b, h, 64-row tile), the forward's decomposition (two waves per
-//                SIMD).  For every key
-//                tile it sees: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
-//                dQ^T += K^T dS^T.  Deterministic (each dQ element has one writer).
+//                SIMD).  For every key tile it sees: S^T = K Q^T, dP^T = V dO^T,
+//                dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.  K and V tiles arrive by
+//                direct loads into LDS.  Deterministic (each dQ element has one writer).
+//
+// Every staging buffer is its own LDS object and both loops are unrolled by two, so the
+// buffer a step reads is known at compile time to differ from the one the direct loads of
+// the next step fill; the loads then stay in flight across the step's compute.
 //
 // The recompute of P from the saved log-sum-exp and dS = P * (dO V^T - D) follow the
 // FlashAttention-3 backward entry of the "SnapKitty Transformer 8B" model card
 // (Protected Inventions); that entry reduces dQ with atomics across query tiles, which
 // this library replaces by the separate deterministic dQ pass.
+#include <type_traits>
+
 #include "gqa_device.h"
 
 namespace gqa {
@@ -63,15 +71,31 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   if (row < rows && part == 0) p.out_delta[row] = acc;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS staging: buffer_load_dwordx4 ... lds writes lane i's 16 bytes to M0 + 16 i,
+// so each lane picks the global chunk that belongs in its LDS slot.  Instruction j (0..7)
+// fills LDS rows 8j..8j+7 of a row-major tile; this is the lane's byte offset inside the
+// tile's global rows.
+__device__ __forceinline__ int direct_voff(int j, int lane) {
+  const int r = 8 * j + (lane >> 3);
+  return r * 128 + (((lane & 7) ^ swz(r)) << 4);
+}
+
 // ------------------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------------------
 struct DkdvStage {
   char q_rm[8192];   // Q tile, row-major (rows = queries)
   char do_rm[8192];  // dO tile, row-major
-  float lse2[64];    // lse * log2(e); +inf past the end of the sequence (P = 0 there)
-  float ndelta[64];  // -delta; 0 past the end
+  float lse[256];    // lse of the tile's 64 rows (entries 64.. are load padding); 0 past the end
+  float delta[256];  // delta, likewise
 };
+
+// The two staging buffers of the dK/dV pass, as distinct LDS objects so that the compiler
+// can tell the buffer being read from the one the direct loads are filling.
+__shared__ __attribute__((aligned(1024))) DkdvStage g_dkdv_stage0;
+__shared__ __attribute__((aligned(1024))) DkdvStage g_dkdv_stage1;
 
 // Per-wave state of the dK/dV pass: 32 keys (one column block) of one kv head.
 template <int DT>
@@ -80,22 +104,23 @@ struct DkdvWave {
   int kw0, kw1;
   MaskSpec m;
   float c2;
-  u32x4 kf[4], vf[4];  // K and V rows as B operands [contraction step]
+  u32x4 kf[4], vf[4];  // K and -V rows as B operands [contraction step]
   f32x16 dk[2], dv[2];  // transposed accumulators [d block]
 
   // one 32-query block qb of the staged tile (rows qr0 ..): both products for dK and dV
   template <bool PRECISE>
   __device__ __forceinline__ void block(const DkdvStage& sb, int qb, int qr0, bool partial) {
     f32x16 s, dp;
-    f32x16 nd;  // -delta of this lane's 16 rows: the initial dP accumulator, so dP' = dP - delta
+    f32x16 nd;  // delta of this lane's 16 rows: the initial accumulator of dO (-V)^T, which
+                // therefore holds delta - dP, and dS = P (dP - delta) = -P (delta - dP)
     float L[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 lv = *(const f32x4*)(sb.lse2 + qb * 32 + 8 * r4 + 4 * hl);
-      const f32x4 dv4 = *(const f32x4*)(sb.ndelta + qb * 32 + 8 * r4 + 4 * hl);
+      const f32x4 lv = *(const f32x4*)(sb.lse + qb * 32 + 8 * r4 + 4 * hl);
+      const f32x4 dv4 = *(const f32x4*)(sb.delta + qb * 32 + 8 * r4 + 4 * hl);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        L[4 * r4 + x] = lv[x];
+        L[4 * r4 + x] = lv[x] * kLog2e;
         nd[4 * r4 + x] = dv4[x];
       }
     }
@@ -129,7 +154,7 @@ struct DkdvWave {
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * t + e;
         pv[e] = exp2_fast(__builtin_fmaf(s[r], c2, -L[r]));
-        dsv[e] = pv[e] * dp[r];
+        dsv[e] = -pv[e] * dp[r];
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -157,11 +182,39 @@ struct DkdvWave {
   }
 };
 
+// Wave-uniform copies of the parameters: the out-of-line pass receives them in vector
+// registers, and buffer descriptors built from non-uniform values turn every buffer load
+// into a waterfall loop.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+template <typename T>
+__device__ __forceinline__ T* uni(T* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)((hi << 32) | lo);
+}
+__device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
+  BwdParams p;
+  p.q = uni(in.q); p.k = uni(in.k); p.v = uni(in.v); p.o = uni(in.o); p.o_lo = uni(in.o_lo);
+  p.d_o = uni(in.d_o); p.lse = uni(in.lse); p.delta = uni(in.delta); p.out_delta = uni(in.out_delta);
+  p.dq = uni(in.dq); p.dk = uni(in.dk); p.dv = uni(in.dv);
+  p.B = uni(in.B); p.H = uni(in.H); p.G = uni(in.G); p.S = uni(in.S);
+  p.scale = uni(in.scale); p.scale_log2 = uni(in.scale_log2);
+  p.mask.S = uni(in.mask.S); p.mask.causal = uni(in.mask.causal);
+  p.mask.window = uni(in.mask.window); p.mask.sinks = uni(in.mask.sinks);
+  p.hpw = uni(in.hpw); p.qpw = uni(in.qpw); p.n_qblk = uni(in.n_qblk); p.n_kblk = uni(in.n_kblk);
+  return p;
+}
+
 // The whole dK/dV pass for one workgroup.  Kept out of line so that the rare variant for
 // key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
 // allocation instead of raising the common variant's.
 template <int DT, bool PRECISE>
-__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& p, DkdvStage* stage) {
+__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
+  const BwdParams p = uniform_params(pin);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -193,75 +246,68 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& p, DkdvSta
   for (int ks = 0; ks < 4; ++ks) {
     const int off = (W.kw0 + W.l32) * 128 + ks * 32 + W.hl * 16;
     W.kf[ks] = buf_load16(krs, off);
-    W.vf[ks] = buf_load16(vrs, off);
+    W.vf[ks] = buf_load16(vrs, off) ^ 0x80008000u;  // -V: flip both 16-bit signs
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K/V operands are in registers before the loop
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     W.dk[db] = f32x16{};
     W.dv[db] = f32x16{};
   }
 
-  // staging roles: threads 0..127 stage Q tiles, 128..255 dO tiles (row-major);
-  // threads 256..319 stage lse (log2 units), 320..383 -delta.
-  const int kind = wave >> 1;  // 0: Q, 1: dO, 2..3: statistics
-  const int unit = tid & 127;
-  const int ur0 = (unit >> 3) * 4;
-  const int udc = unit & 7;
-  const int flip = (unit >> 3) & 1;
-  Unit st;
-  float st_f = 0.f;
-
+  // Staging by direct loads into LDS (no registers): wave w loads LDS rows 8w..8w+7 of the
+  // Q and dO tiles; waves 0 and 1 load the lse and delta rows (a full 1 KiB load each, of
+  // which the first 64 entries are the tile's).  Rows past the end of the sequence read
+  // zero, which makes their P V and dS contributions vanish (Q and dO rows are zero).
+  const int voff = direct_voff(wave, lane);
   const TileRanges tr = query_tiles_for_keys(W.m, K0, K1);
   const int nq = tr.count();
   const int n_iter = nq * hpg;
-  auto load_stage = [&](int iter) __attribute__((always_inline)) {
+  auto stage_dma = [&](DkdvStage* sb, int iter) __attribute__((always_inline)) {
     const int hh = iter / nq;
     const int qt = tr.tile(iter % nq);
     const size_t slab = (size_t)(b * p.H + g * hpg + hh) * S;
-    if (kind < 2) {
-      const __amdgpu_buffer_rsrc_t r =
-          slab_rsrc((const uint16_t*)(kind == 0 ? p.q : p.d_o) + slab * kHeadDim, S);
-      unit_load_buf_rm(st, r, qt * kTile + ur0, udc, flip);
-    } else if (tid < 384) {
-      const int i = qt * kTile + (tid & 63);
-      if (tid < 320)
-        st_f = (i < S) ? p.lse[slab + i] * kLog2e : INFINITY;
-      else
-        st_f = (i < S) ? -p.delta[slab + i] : 0.f;
+    const __amdgpu_buffer_rsrc_t qr = slab_rsrc((const uint16_t*)p.q + slab * kHeadDim, S);
+    const __amdgpu_buffer_rsrc_t dr = slab_rsrc((const uint16_t*)p.d_o + slab * kHeadDim, S);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(sb->q_rm + 1024 * wave), 16, qt * kTile * 128 + voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 1024 * wave), 16, qt * kTile * 128 + voff, 0, 0, 0);
+    if (wave < 2) {
+      const float* base = (wave == 0 ? p.lse : p.delta) + slab;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, S * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(wave == 0 ? sb->lse : sb->delta), 16,
+                                               (qt * kTile + 4 * lane) * 4, 0, 0, 0);
     }
   };
-  auto store_stage = [&](int buf) __attribute__((always_inline)) {
-    DkdvStage& sb = stage[buf];
-    if (kind < 2)
-      unit_store_rm_flip(kind == 0 ? sb.q_rm : sb.do_rm, st, ur0, udc, flip);
-    else if (tid < 320)
-      sb.lse2[tid - 256] = st_f;
-    else if (tid < 384)
-      sb.ndelta[tid - 320] = st_f;
-  };
-
-  if (n_iter > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int qt = tr.tile(it % nq);
-    const bool more = it + 1 < n_iter;
-    if (more) load_stage(it + 1);
-    const DkdvStage& sb = stage[it & 1];
-    if (active) {
+  auto compute = [&](const DkdvStage& sb, int iter) __attribute__((always_inline)) {
+    if (!active) return;
+    const int qt = tr.tile(iter % nq);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qr0 = qt * kTile + qb * 32;
-        const int cls = qr0 < S ? classify(W.m, qr0, imin(qr0 + 31, S - 1), W.kw0, W.kw1) : (int)kEmpty;
-        if (cls == kEmpty) continue;
-        W.template block<PRECISE>(sb, qb, qr0, cls != kFull);
-      }
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qr0 = qt * kTile + qb * 32;
+      const int cls = qr0 < S ? classify(W.m, qr0, imin(qr0 + 31, S - 1), W.kw0, W.kw1) : (int)kEmpty;
+      if (cls == kEmpty) continue;
+      W.template block<PRECISE>(sb, qb, qr0, cls != kFull);
     }
-    if (more) store_stage((it + 1) & 1);
-    __syncthreads();
+  };
+
+  if (n_iter > 0) stage_dma(&g_dkdv_stage0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // unrolled by two so that every LDS buffer is known at compile time (the loads into the
+  // other buffer then need no wait before this buffer's reads)
+  auto iter_body = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    if (it + 1 < n_iter) stage_dma(P ? &g_dkdv_stage0 : &g_dkdv_stage1, it + 1);
+    compute(P ? g_dkdv_stage1 : g_dkdv_stage0, it);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): next stage landed, reads done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    iter_body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 >= n_iter) break;
+    iter_body(std::integral_constant<int, 1>{}, it + 1);
   }
 
   if (!active) return;
@@ -284,25 +330,27 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& p, DkdvSta
 
 template <int DT>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) DkdvStage stage[2];
   // Sink keys collect attention from every later query, so their dK and dV are sums of
   // many large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value
   // plus its rounded residual (two products each), which keeps their rounding out of the sum.
   const int kblk = (int)(blockIdx.x / (p.B * p.G));
   if (p.mask.window > 0 && kblk * 4 * kTile < p.mask.sinks)
-    dkdv_block<DT, true>(p, stage);
+    dkdv_block<DT, true>(p);
   else
-    dkdv_block<DT, false>(p, stage);
+    dkdv_block<DT, false>(p);
 }
 
 // ------------------------------------------------------------------------------------
 // dQ
 // ------------------------------------------------------------------------------------
+// The staging buffers of the dQ pass (distinct LDS objects, see the dK/dV pass).
+__shared__ __attribute__((aligned(1024))) char g_dq_k0[8192];
+__shared__ __attribute__((aligned(1024))) char g_dq_k1[8192];
+__shared__ __attribute__((aligned(1024))) char g_dq_v0[8192];
+__shared__ __attribute__((aligned(1024))) char g_dq_v1[8192];
+
 template <int DT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char k_lds[2][8192];  // row-major K tiles
-  __shared__ __attribute__((aligned(16))) char v_lds[2][8192];  // row-major V tiles
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -330,6 +378,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim, S);
   const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim, S);
 
+  const TileRanges tr = key_tiles_for_rows(m, Q0, Q1);
+  const int nt = tr.count();
+  // rows of key tile n; past the last tile, row S (all loads out of range: zero, no traffic)
+  auto tile_row = [&](int n) __attribute__((always_inline)) { return n < nt ? tr.tile(n) * kTile : S; };
+  // direct loads: wave w fills LDS rows 16w..16w+15 of the K and V tiles
+  const int dvo[2] = {direct_voff(2 * wave, lane), direct_voff(2 * wave + 1, lane)};
+  auto stage = [&](char* kt, char* vt, int row0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + 1024 * (2 * wave + u)), 16, row0 * 128 + dvo[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vt + 1024 * (2 * wave + u)), 16, row0 * 128 + dvo[u], 0, 0, 0);
+    }
+  };
+  stage(g_dq_k0, g_dq_v0, tile_row(0));
+
   u32x4 qf[2][4], df[2][4];
   float lse2[2], dlt[2];
 #pragma unroll
@@ -352,95 +415,112 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) dq[db][cb] = f32x16{};
 
-  // staging roles: threads 0..127 stage K tiles, 128..255 V tiles (row-major)
-  const int kind = wave >> 1;
-  const int unit = tid & 127;
-  const int ur0 = (unit >> 3) * 4;
-  const int udc = unit & 7;
-  const int flip = (unit >> 3) & 1;
-  Unit st;
-
-  const TileRanges tr = key_tiles_for_rows(m, Q0, Q1);
-  const int nt = tr.count();
+  // lane offsets of the LDS operand reads (the swizzle depends on row bits 0..3 only, so the
+  // key-half, step and buffer offsets are additive constants)
+  int koff[4], toff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = rm_off(l32, ks * 2 + hl);
+  {
+    const int r0 = 4 * hl + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int c0 = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      toff[db][0] = rm_off(r0, c0 >> 3) + (c0 & 7) * 2;
+      toff[db][1] = rm_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
+    }
+  }
+  // a key half [k, k + 31] is fully visible to all 64 rows iff these hold
+  const int lim_hi = m.causal ? imin(q0, S - 1) : S - 1;
+  const int win_lo = m.window > 0 ? q1 - m.window + 1 : -(1 << 30);
   const float c2 = p.scale_log2;
-  auto tile_row = [&](int n) __attribute__((always_inline)) { return n < nt ? tr.tile(n) * kTile : S; };
-
-  unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(0) + ur0, udc, flip);
-  unit_store_rm_flip(kind == 0 ? k_lds[0] : v_lds[0], st, ur0, udc, flip);
+  __builtin_amdgcn_s_waitcnt(0);  // Q, dO operands and the first K/V tiles have landed
   __syncthreads();
 
-  for (int it = 0; it < nt; ++it) {
-    const int k0 = tr.tile(it) * kTile;
-    unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(it + 1) + ur0, udc, flip);
-    const char* kl = k_lds[it & 1];
-    const char* vl = v_lds[it & 1];
-    if (active) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  auto half = [&](const char* kl, const char* vl, int kb, int kr0) __attribute__((always_inline)) {
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kr0 = k0 + kb * 32;
-        const int cls = kr0 < S ? classify(m, q0, q1, kr0, kr0 + 31) : (int)kEmpty;
-        if (cls == kEmpty) continue;
-        f32x16 s[2], dp[2];
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 ak = *(const u32x4*)(kl + kb * 4096 + koff[ks]);
+      const u32x4 av = *(const u32x4*)(vl + kb * 4096 + koff[ks]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 ak = lds_rm_operand(kl, kb, ks, l32, hl);
-          const u32x4 av = lds_rm_operand(vl, kb, ks, l32, hl);
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            s[cb] = mfma32<DT>(ak, qf[cb][ks], ks == 0 ? f32x16{} : s[cb]);
-            dp[cb] = mfma32<DT>(av, df[cb][ks], ks == 0 ? f32x16{} : dp[cb]);
-          }
-        }
-        if (__builtin_expect(cls != kFull, 0)) {
-          // lane = query column i, register r = key kr0 + 4*hl + rr(r)
-          const int base = kr0 + 4 * hl;
-          const int kmax = m.S - 1 - base;
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const int i = q0 + cb * 32 + l32;
-            const int causal_hi = m.causal ? i - base : kmax;
-            const int hi = causal_hi < kmax ? causal_hi : kmax;
-            const int win_lo = m.window > 0 ? i - m.window + 1 - base : -(1 << 30);
-            const int sink_hi = m.sinks - 1 - base;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = 8 * (r >> 2) + (r & 3);
-              const bool ok = (rr <= hi) && (rr >= win_lo || rr <= sink_hi);
-              s[cb][r] = ok ? s[cb][r] : -INFINITY;
-            }
-          }
-        }
-        u32x4 pds[2][2];  // [cb][t]
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            float dsv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * t + e;
-              const float pv = exp2_fast(__builtin_fmaf(s[cb][r], c2, -lse2[cb]));
-              dsv[e] = pv * (dp[cb][r] - dlt[cb]);
-            }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) pds[cb][t][w] = pack2<DT>(dsv[2 * w], dsv[2 * w + 1]);
-          }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const u32x4 akt = lds_rm_transposed_operand(kl, db, kb, t, lane);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) dq[db][cb] = mfma32<DT>(akt, pds[cb][t], dq[db][cb]);
-          }
+      for (int cb = 0; cb < 2; ++cb) {
+        s[cb] = mfma32<DT>(ak, qf[cb][ks], ks == 0 ? f32x16{} : s[cb]);
+        dp[cb] = mfma32<DT>(av, df[cb][ks], ks == 0 ? f32x16{} : dp[cb]);
       }
     }
-    unit_store_rm_flip(kind == 0 ? k_lds[(it + 1) & 1] : v_lds[(it + 1) & 1], st, ur0, udc, flip);
-    __syncthreads();
+    if (__builtin_expect(!(kr0 + 31 <= lim_hi && (kr0 >= win_lo || kr0 + 31 < m.sinks)), 0)) {
+      // lane = query column i, register r = key kr0 + 4*hl + rr(r)
+      const int base = kr0 + 4 * hl;
+      const int kmax = m.S - 1 - base;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int i = q0 + cb * 32 + l32;
+        const int causal_hi = m.causal ? i - base : kmax;
+        const int hi = causal_hi < kmax ? causal_hi : kmax;
+        const int wlo = m.window > 0 ? i - m.window + 1 - base : -(1 << 30);
+        const int sink_hi = m.sinks - 1 - base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + (r & 3);
+          const bool ok = (rr <= hi) && (rr >= wlo || rr <= sink_hi);
+          s[cb][r] = ok ? s[cb][r] : -INFINITY;
+        }
+      }
+    }
+    u32x4 pds[2][2];  // [cb][t]
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * t + e;
+          const float pv = exp2_fast(__builtin_fmaf(s[cb][r], c2, -lse2[cb]));
+          dsv[e] = pv * (dp[cb][r] - dlt[cb]);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pds[cb][t][w] = pack2<DT>(dsv[2 * w], dsv[2 * w + 1]);
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const char* base = kl + (kb * 32 + 16 * t) * 128;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + toff[db][0]));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + toff[db][1]));
+        const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+        const u32x4 akt = u32x4{ux[0], ux[1], uy[0], uy[1]};
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) dq[db][cb] = mfma32<DT>(akt, pds[cb][t], dq[db][cb]);
+      }
+  };
+  // one key tile; PAR = it % 2 fixes the LDS buffers at compile time
+  auto tile = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    char* kc = P ? g_dq_k1 : g_dq_k0;
+    char* vc = P ? g_dq_v1 : g_dq_v0;
+    stage(P ? g_dq_k0 : g_dq_k1, P ? g_dq_v0 : g_dq_v1, tile_row(it + 1));
+    const int k0 = tr.tile(it) * kTile;
+    if (active) {
+      half(kc, vc, 0, k0);
+      if (k0 + 32 < S) half(kc, vc, 1, k0 + 32);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): next tiles landed, reads done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  for (int it = 0; it < nt; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 >= nt) break;
+    tile(std::integral_constant<int, 1>{}, it + 1);
   }
 
   if (!active) return;
-  float* dqslab = p.dq + qslab_rows * kHeadDim;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int i = q0 + cb * 32 + l32;
