@@ -5,26 +5,28 @@
 // head h (hpw heads x qpw row tiles per workgroup; all heads belong to kv group g, so every
 // wave reads the same K/V tiles).  The workgroup walks the key tiles that hold at least
 // one visible key: sink tiles, then the window/causal range; everything between is never
-// loaded.  K and V tiles are staged row-major into LDS, double-buffered: the next tile's
-// buffer loads (which read zero past the end of the sequence) are issued before this
-// tile's math and written after it, one barrier per tile.
+// loaded.  K and V tiles arrive by direct loads into LDS (buffer_load ... lds, no staging
+// registers; rows past the end of the sequence read zero), triple-buffered with one
+// barrier per tile.
 //
 // Per wave, S^T = K Q^T runs on v_mfma_f32_32x32x16 with the wave's Q tile held in
 // registers as the B operand, so each accumulator lane holds one query column: row
-// statistics are in-lane plus one exchange between the two 32-lane halves.  All scores of
-// a 64-key tile are issued first; one running-maximum decision covers the tile; then the
-// probabilities of the first 32-key half feed O^T += V^T P^T on the matrix cores while the
-// VALU exponentiates the second half.  V^T operands come from the row-major V tile through
-// ds_read_b64_tr_b16 transposed reads, and P^T straight from the S^T accumulator registers
-// (see gqa_device.h).  The online softmax runs in fp32: exp2 with scale*log2(e) folded into
-// one FMA, row sums of the unrounded P in fp32 (so lse keeps fp32 accuracy), and a running
-// maximum that is only raised when a tile's maximum exceeds it by more than 2^8, so the O
-// rescale is skipped on almost every tile and P stays below 2^8.  Halves that are not fully
-// visible are masked with one compare per element against per-lane bounds.
+// statistics are in-lane plus one exchange between the two 32-lane halves.  The loop is a
+// software pipeline over 32-key halves: while the VALU exponentiates one half, the matrix
+// cores compute the scores of the next, then the half's probabilities feed
+// O^T += V^T P^T.  V^T operands come from the row-major V tile through ds_read_b64_tr_b16
+// transposed reads, and P^T straight from the S^T accumulator registers (see
+// gqa_device.h).  The online softmax runs in fp32: exp2 with scale*log2(e) folded into one
+// FMA, row sums of the unrounded P in fp32 (so lse keeps fp32 accuracy), and a running
+// maximum that is only raised when a half's maximum exceeds it by more than 2^8, so the O
+// rescale is skipped on almost every half and P stays below 2^8.  Halves that are not
+// fully visible are masked with one compare per element against per-lane bounds.
 //
 // The online softmax with running max and sum and the fused score/softmax/PV loop follow
 // the "SnapKitty Transformer 8B" model card's FlashAttention Kernel section; the tiling,
 // operand orientation and staging here are this library's own for CDNA4.
+#include <type_traits>
+
 #include "gqa_device.h"
 
 namespace gqa {
@@ -46,13 +48,31 @@ struct FwdWave {
   float mrow[2];    // running maximum (log2 units) per column block
   float lrow[2];    // running sum (this lane's half of the keys)
   float alpha[2];   // rescale factor decided by the last softmax
+  float nmuse[2];   // -mrow, or 0 while the row has seen no visible key (mrow = -inf)
+  int lim_hi;       // a key half [k, k + 31] is fully visible to all 64 rows iff
+  int win_lo;       //   k + 31 <= lim_hi && (k >= win_lo || k + 31 < m.sinks)
   bool rescale;     // wave-uniform: the last softmax raised the maximum
+  int koff[4];      // lane's byte offset of the K operand, contraction step ks (block 0)
+  int voff[2][2];   // lane's byte offset of the transposed V read [d block][second row group]
 
-  // S^T[cb] = K[kb] Q^T[cb] for key half kb of the tile in `kl` (row-major LDS tile)
+  __device__ __forceinline__ void init_offsets() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = rm_off(l32, ks * 2 + hl);
+    const int r0 = 4 * hl + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int c0 = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff[db][0] = rm_off(r0, c0 >> 3) + (c0 & 7) * 2;
+      voff[db][1] = rm_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
+    }
+  }
+
+  // S^T[cb] = K[kb] Q^T[cb] for key half kb of the tile in `kl` (row-major LDS tile); the
+  // swizzle depends on row bits 0..3 only, so the block offset is an additive constant
   __device__ __forceinline__ void scores(const char* kl, int kb, f32x16 (&s)[2]) const {
     u32x4 a[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = lds_rm_operand(kl, kb, ks, l32, hl);
+    for (int ks = 0; ks < 4; ++ks) a[ks] = *(const u32x4*)(kl + kb * 4096 + koff[ks]);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32<DT>(a[0], qf[cb][0], f32x16{});
 #pragma unroll
@@ -62,19 +82,32 @@ struct FwdWave {
   }
 
   // O^T[db][cb] += V^T[db] P^T[cb] over key half kb of the tile in `vl` (row-major tile,
-  // read transposed)
+  // read transposed: rows 32 kb + 16 t + {0..3, 8..11} + 4 h, see lds_rm_transposed_operand)
   __device__ __forceinline__ void accumulate(const char* vl, int kb, const u32x4 (&pf)[2][2]) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     u32x4 a[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) a[db][t] = lds_rm_transposed_operand(vl, db, kb, t, lane);
+      for (int db = 0; db < 2; ++db) {
+        const char* base = vl + (kb * 32 + 16 * t) * 128;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + voff[db][0]));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + voff[db][1]));
+        const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+        a[db][t] = u32x4{ux[0], ux[1], uy[0], uy[1]};
+      }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) o[db][cb] = mfma32<DT>(a[db][t], pf[cb][t], o[db][cb]);
+  }
+
+  __device__ __forceinline__ bool half_full(int k) const {
+    return k + 31 <= lim_hi && (k >= win_lo || k + 31 < m.sinks);
   }
 
   // hide keys that are not visible (halves that are not fully visible only).  Register r of
@@ -99,27 +132,32 @@ struct FwdWave {
     }
   }
 
-  // running-maximum update for one 64-key tile (both halves): sets rescale/alpha/mrow
-  __device__ __forceinline__ void decide(const f32x16 (&s0)[2], const f32x16 (&s1)[2]) {
+  // running-maximum update for one 32-key half (already masked): sets rescale and, when the
+  // maximum is raised, alpha/mrow/lrow (rare)
+  __device__ __forceinline__ void decide(const f32x16 (&s)[2]) {
     float mx[2];
     bool need = false;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      float a = vmax(s0[cb][0], s0[cb][1]);
+      float a = vmax(s[cb][0], s[cb][1]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) a = vmax(vmax(a, s0[cb][r]), s0[cb][r + 1]);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) a = vmax(vmax(a, s1[cb][r]), s1[cb][r + 1]);
-      mx[cb] = max_across_halves(a) * c2;
+      for (int r = 2; r < 16; r += 2) a = vmax(vmax(a, s[cb][r]), s[cb][r + 1]);
+      uint32_t u = __builtin_bit_cast(uint32_t, a);
+      auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx[cb] = vmax(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1])) * c2;
       need = need || (mx[cb] > mrow[cb] + kRescaleThreshold);
     }
     rescale = wave_any(need);
+    if (__builtin_expect(rescale, 0)) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float mnew = rescale ? vmax(mrow[cb], mx[cb]) : mrow[cb];
-      alpha[cb] = (rescale && mnew != -INFINITY) ? exp2_fast(mrow[cb] - mnew) : 1.0f;
-      mrow[cb] = mnew;
-      lrow[cb] *= alpha[cb];
+      for (int cb = 0; cb < 2; ++cb) {
+        const float mnew = vmax(mrow[cb], mx[cb]);
+        alpha[cb] = mnew != -INFINITY ? exp2_fast(mrow[cb] - mnew) : 1.0f;
+        mrow[cb] = mnew;
+        nmuse[cb] = mnew == -INFINITY ? 0.f : -mnew;
+        lrow[cb] *= alpha[cb];
+      }
+      apply_rescale();
     }
   }
 
@@ -127,13 +165,12 @@ struct FwdWave {
   __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const float muse = (mrow[cb] == -INFINITY) ? 0.f : mrow[cb];
       float lsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[cb][8 * t + e], c2, -muse));
+        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[cb][8 * t + e], c2, nmuse[cb]));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           pf[cb][t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
@@ -155,10 +192,49 @@ struct FwdWave {
   }
 };
 
+// Direct-to-LDS staging: buffer_load_dwordx4 ... lds writes lane i's 16 bytes to M0 + 16 i,
+// so each lane picks the global chunk that belongs in its LDS slot.  Instruction j (0..7)
+// fills LDS rows 8j..8j+7 of a tile; this returns the lane's byte offset inside the tile's
+// global rows for instruction j.
+__device__ __forceinline__ int direct_voff(int j, int lane) {
+  const int r = 8 * j + (lane >> 3);
+  return r * 128 + (((lane & 7) ^ swz(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier for LDS filled only by direct loads: wait until at most VM of this
+// wave's vector-memory operations are outstanding and its LDS reads have returned, then
+// s_barrier.  (__syncthreads would also drain the younger direct loads, which are meant to
+// stay in flight across the barrier.)  The empty asm keeps the compiler from moving LDS
+// accesses across it.
+template <int VM>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(VM >= 0 && VM < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wave `wave` stages LDS rows 16*wave .. 16*wave + 15 of the tile starting at global row
+// `row0` (rows at or past the end of the slab read as zero).
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t rs, char* tile, int row0, const int (&voff)[2],
+                                           int wave) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + 1024 * (2 * wave + u)), 16,
+                                             row0 * 128 + voff[u], 0, 0, 0);
+}
+
 template <int DT>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) char k_lds[2][8192];
-  __shared__ __attribute__((aligned(16))) char v_lds[2][8192];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[8192];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[8192];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[8192];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[8192];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[8192];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[8192];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,10 +258,22 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   W.q1 = imin(W.q0 + kTile - 1, S - 1);
   W.m = p.mask;
   W.c2 = p.scale_log2;
+  W.init_offsets();
   const bool active = W.q0 < S;
   const __amdgpu_buffer_rsrc_t qrs = slab_rsrc((const uint16_t*)p.q + (size_t)(b * p.H + h) * S * kHeadDim, S);
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim, S);
   const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const uint16_t*)p.v + (size_t)(b * p.G + g) * S * kHeadDim, S);
+
+  const TileRanges tr = key_tiles_for_rows(W.m, Q0, Q1);
+  const int nt = tr.count();
+  const int voff[2] = {direct_voff(2 * wave, lane), direct_voff(2 * wave + 1, lane)};
+  // rows of key tile n; past the last tile, row S: every load is out of range and fills zeros
+  auto tile_row = [&](int n) __attribute__((always_inline)) { return n < nt ? tr.tile(n) * kTile : S; };
+
+  stage_rows(krs, k_lds0, tile_row(0), voff, wave);
+  stage_rows(vrs, v_lds0, tile_row(0), voff, wave);
+  stage_rows(krs, k_lds1, tile_row(1), voff, wave);
+
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -198,38 +286,55 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   W.mrow[0] = W.mrow[1] = -INFINITY;
   W.lrow[0] = W.lrow[1] = 0.f;
   W.alpha[0] = W.alpha[1] = 1.f;
+  W.nmuse[0] = W.nmuse[1] = 0.f;
+  W.lim_hi = W.m.causal ? imin(W.q0, S - 1) : S - 1;
+  W.win_lo = W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30);
   W.rescale = false;
 
-  const TileRanges tr = key_tiles_for_rows(W.m, Q0, Q1);
-  const int nt = tr.count();
-  const int kind = wave >> 1;
-  const int unit = tid & 127;
-  const int ur0 = (unit >> 3) * 4;
-  const int udc = unit & 7;
-  Unit st;
-  auto tile_row = [&](int n) __attribute__((always_inline)) { return n < nt ? tr.tile(n) * kTile : S; };
-
-  const int flip = (unit >> 3) & 1;  // alternate row order by unit parity
-  unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(0) + ur0, udc, flip);
-  unit_store_rm_flip(kind == 0 ? k_lds[0] : v_lds[0], st, ur0, udc, flip);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int n = 0; n < nt; ++n) {
-    unit_load_buf_rm(st, kind == 0 ? krs : vrs, tile_row(n + 1) + ur0, udc, flip);
+  // Half-tile software pipeline.  A step softmaxes one 32-key half while the matrix cores
+  // compute the scores of the following half, then adds that half's P V; so tile n reads
+  // K_n and K_{n+1} and V_n.  K and V tiles are triple-buffered (buffer n % 3) and the loop
+  // is unrolled by three, so every buffer is fixed at compile time.  One barrier per tile:
+  // right after it, the direct loads of K_{n+2} and V_{n+1} go into the buffers of K_{n-1}
+  // and V_{n-2}, which no wave reads any more; they have the whole tile to land and the
+  // next barrier drains them, so nothing is in flight across the loop's back edge.  Loads
+  // past the last tile read zeros (no traffic), which keeps the steps unconditional.
+  f32x16 sc[2], sn[2];  // S^T of the half being softmaxed / the next half, [column block]
+  W.scores(k_lds0, 0, sc);
+
+  auto tile = [&](auto par, int n) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    char* kn = P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2;    // K_n
+    char* kn1 = P == 0 ? k_lds1 : P == 1 ? k_lds2 : k_lds0;   // K_{n+1}
+    char* kn2 = P == 0 ? k_lds2 : P == 1 ? k_lds0 : k_lds1;   // receives K_{n+2}
+    char* vn = P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2;    // V_n
+    char* vn1 = P == 0 ? v_lds1 : P == 1 ? v_lds2 : v_lds0;   // receives V_{n+1}
     const int k0 = tr.tile(n) * kTile;
-    f32x16 s0[2], s1[2];
-    u32x4 p0[2][2], p1[2][2];
-    W.scores(k_lds[n & 1], 0, s0);
-    W.scores(k_lds[n & 1], 1, s1);
-    if (__builtin_expect(classify(W.m, W.q0, W.q1, k0, k0 + 31) != kFull, 0)) W.mask(s0, k0);
-    if (__builtin_expect(classify(W.m, W.q0, W.q1, k0 + 32, k0 + 63) != kFull, 0)) W.mask(s1, k0 + 32);
-    W.decide(s0, s1);
-    if (__builtin_expect(W.rescale, 0)) W.apply_rescale();
-    W.probs(s0, p0);
-    W.accumulate(v_lds[n & 1], 0, p0);
-    W.probs(s1, p1);
-    W.accumulate(v_lds[n & 1], 1, p1);
-    unit_store_rm_flip(kind == 0 ? k_lds[(n + 1) & 1] : v_lds[(n + 1) & 1], st, ur0, udc, flip);
-    __syncthreads();
+    u32x4 pf[2][2];
+    stage_rows(krs, kn2, tile_row(n + 2), voff, wave);
+    stage_rows(vrs, vn1, tile_row(n + 1), voff, wave);
+    // half 0: scores of (n, 1) while exponentiating (n, 0)
+    W.scores(kn, 1, sn);
+    if (__builtin_expect(!W.half_full(k0), 0)) W.mask(sc, k0);
+    W.decide(sc);
+    W.probs(sc, pf);
+    W.accumulate(vn, 0, pf);
+    // half 1: scores of (n + 1, 0) while exponentiating (n, 1)
+    W.scores(kn1, 0, sc);
+    if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.mask(sn, k0 + 32);
+    W.decide(sn);
+    W.probs(sn, pf);
+    W.accumulate(vn, 1, pf);
+    lds_barrier<0>();  // this tile's loads have landed; its buffers are read no more
+  };
+  for (int n = 0; n < nt; n += 3) {
+    tile(std::integral_constant<int, 0>{}, n);
+    if (n + 1 >= nt) break;
+    tile(std::integral_constant<int, 1>{}, n + 1);
+    if (n + 2 >= nt) break;
+    tile(std::integral_constant<int, 2>{}, n + 2);
   }
 
   if (!active) return;
