@@ -14,13 +14,18 @@
 // statistics are in-lane plus one exchange between the two 32-lane halves.  The loop is a
 // software pipeline over 32-key halves: while the VALU exponentiates one half, the matrix
 // cores compute the scores of the next, then the half's probabilities feed
-// O^T += V^T P^T.  V^T operands come from the row-major V tile through ds_read_b64_tr_b16
-// transposed reads, and P^T straight from the S^T accumulator registers (see
-// gqa_device.h).  The online softmax runs in fp32: exp2 with scale*log2(e) folded into one
-// FMA, row sums of the unrounded P in fp32 (so lse keeps fp32 accuracy), and a running
-// maximum that is only raised when a half's maximum exceeds it by more than 2^8, so the O
-// rescale is skipped on almost every half and P stays below 2^8.  Halves that are not
-// fully visible are masked with one compare per element against per-lane bounds.
+// O^T += V^T P^T.  Operands are read from LDS one step ahead of their MFMAs.  V^T
+// operands come from the row-major V tile through ds_read_b64_tr_b16 transposed reads, and
+// P^T straight from the S^T accumulator registers (see gqa_device.h).
+//
+// Online softmax in fp32: exp2 with scale*log2(e) folded into one FMA and row sums of the
+// unrounded P in fp32 (so lse keeps fp32 accuracy).  The running maximum only keeps exp2
+// in range, so a half is exponentiated against it without computing the half's own
+// maximum; a lane's partial row sum above 2^16 (or a row with no maximum yet) sends the
+// half through the exact path: take its maximum, raise the running maximum when it grew by
+// more than 2^8, rescale O and the sums, exponentiate again.  P thus stays below 2^16,
+// which the rounded operands and fp32 sums carry at full relative precision.  Halves that
+// are not fully visible are masked with one compare per element against per-lane bounds.
 //
 // The online softmax with running max and sum and the fused score/softmax/PV loop follow
 // the "SnapKitty Transformer 8B" model card's FlashAttention Kernel section; the tiling,
@@ -34,6 +39,10 @@ namespace gqa {
 namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// A half's exponentials are taken against the running maximum without looking at the
+// half's own maximum; if a lane's partial row sum exceeds this (some P > 2^16 / 16, or an
+// overflow), the half is redone after a proper maximum decision.
+constexpr float kSumGuard = 65536.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Per-wave state and the pieces of one key tile, processed as two 32-key halves.
@@ -67,12 +76,14 @@ struct FwdWave {
     }
   }
 
-  // S^T[cb] = K[kb] Q^T[cb] for key half kb of the tile in `kl` (row-major LDS tile); the
-  // swizzle depends on row bits 0..3 only, so the block offset is an additive constant
-  __device__ __forceinline__ void scores(const char* kl, int kb, f32x16 (&s)[2]) const {
-    u32x4 a[4];
+  // K operands of key half kb of the tile in `kl` (row-major LDS tile); the swizzle depends
+  // on row bits 0..3 only, so the half offset is an additive constant
+  __device__ __forceinline__ void load_k(const char* kl, int kb, u32x4 (&a)[4]) const {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = *(const u32x4*)(kl + kb * 4096 + koff[ks]);
+  }
+  // S^T[cb] = K Q^T[cb] from loaded K operands
+  __device__ __forceinline__ void scores(const u32x4 (&a)[4], f32x16 (&s)[2]) const {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32<DT>(a[0], qf[cb][0], f32x16{});
 #pragma unroll
@@ -81,11 +92,10 @@ struct FwdWave {
       for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32<DT>(a[ks], qf[cb][ks], s[cb]);
   }
 
-  // O^T[db][cb] += V^T[db] P^T[cb] over key half kb of the tile in `vl` (row-major tile,
-  // read transposed: rows 32 kb + 16 t + {0..3, 8..11} + 4 h, see lds_rm_transposed_operand)
-  __device__ __forceinline__ void accumulate(const char* vl, int kb, const u32x4 (&pf)[2][2]) {
+  // V^T operands of key half kb of the tile in `vl` (row-major tile read transposed: rows
+  // 32 kb + 16 t + {0..3, 8..11} + 4 h, see lds_rm_transposed_operand) [d block][step t]
+  __device__ __forceinline__ void load_v(const char* vl, int kb, u32x4 (&a)[2][2]) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    u32x4 a[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -98,6 +108,9 @@ struct FwdWave {
         const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
         a[db][t] = u32x4{ux[0], ux[1], uy[0], uy[1]};
       }
+  }
+  // O^T[db][cb] += V^T[db] P^T[cb] from loaded V operands
+  __device__ __forceinline__ void accumulate(const u32x4 (&a)[2][2], const u32x4 (&pf)[2][2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -106,8 +119,9 @@ struct FwdWave {
         for (int cb = 0; cb < 2; ++cb) o[db][cb] = mfma32<DT>(a[db][t], pf[cb][t], o[db][cb]);
   }
 
+  // wave-uniform (a scalar branch): bitwise tests, then readfirstlane
   __device__ __forceinline__ bool half_full(int k) const {
-    return k + 31 <= lim_hi && (k >= win_lo || k + 31 < m.sinks);
+    return __builtin_amdgcn_readfirstlane((int)(k + 31 <= lim_hi) & ((int)(k >= win_lo) | (int)(k + 31 < m.sinks))) != 0;
   }
 
   // hide keys that are not visible (halves that are not fully visible only).  Register r of
@@ -145,7 +159,7 @@ struct FwdWave {
       uint32_t u = __builtin_bit_cast(uint32_t, a);
       auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
       mx[cb] = vmax(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1])) * c2;
-      need = need || (mx[cb] > mrow[cb] + kRescaleThreshold);
+      need = need | (mx[cb] > mrow[cb] + kRescaleThreshold);
     }
     rescale = wave_any(need);
     if (__builtin_expect(rescale, 0)) {
@@ -162,7 +176,7 @@ struct FwdWave {
   }
 
   // P^T of one half tile at the current maximum, packed into B operands [cb][t]
-  __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
+  __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[2][2], float (&ls)[2]) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       float lsum = 0.f;
@@ -177,8 +191,29 @@ struct FwdWave {
           lsum += pv[2 * w] + pv[2 * w + 1];
         }
       }
-      lrow[cb] += lsum;
+      ls[cb] = lsum;
     }
+  }
+
+  // Softmax of one (masked) half against the running maximum.  The maximum only serves to
+  // keep exp2 in range, so it is left alone unless a lane's partial row sum shows an
+  // exponent above log2(kSumGuard / 16) or the row has no maximum yet (no visible key so
+  // far); then the half's maximum is taken (decide, which raises it and rescales O and the
+  // row sums) and the half is exponentiated again.  P therefore stays below 2^16: the
+  // rounded operands and fp32 sums keep their relative precision at any magnitude.  (Rows
+  // past the end of the sequence may never see a key; they do not hold the slow path.)
+  __device__ __forceinline__ void softmax_half(const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
+    float ls[2];
+    probs(s, pf, ls);
+    // bitwise combination: one ballot, no per-lane branches
+    const bool need = !(ls[0] <= kSumGuard) | !(ls[1] <= kSumGuard) | ((mrow[0] == -INFINITY) & (q0 + l32 < m.S)) |
+                      ((mrow[1] == -INFINITY) & (q0 + 32 + l32 < m.S));
+    if (__builtin_expect(wave_any(need), 0)) {
+      decide(s);
+      probs(s, pf, ls);
+    }
+    lrow[0] += ls[0];
+    lrow[1] += ls[1];
   }
 
   __device__ __forceinline__ void apply_rescale() {
@@ -287,8 +322,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   W.lrow[0] = W.lrow[1] = 0.f;
   W.alpha[0] = W.alpha[1] = 1.f;
   W.nmuse[0] = W.nmuse[1] = 0.f;
-  W.lim_hi = W.m.causal ? imin(W.q0, S - 1) : S - 1;
-  W.win_lo = W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30);
+  W.lim_hi = __builtin_amdgcn_readfirstlane(W.m.causal ? imin(W.q0, S - 1) : S - 1);
+  W.win_lo = __builtin_amdgcn_readfirstlane(W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30));
   W.rescale = false;
 
   __builtin_amdgcn_s_waitcnt(0);
@@ -302,11 +337,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   // next barrier drains them, so nothing is in flight across the loop's back edge.  Loads
   // past the last tile read zeros (no traffic), which keeps the steps unconditional.
   f32x16 sc[2], sn[2];  // S^T of the half being softmaxed / the next half, [column block]
-  W.scores(k_lds0, 0, sc);
+  u32x4 ka[4];           // K operands of the next scores, read one step ahead
+  u32x4 va[2][2];        // V^T operands of this step's P V, read before its softmax
+  W.load_k(k_lds0, 0, ka);
+  W.scores(ka, sc);
+  W.load_k(k_lds0, 1, ka);
 
   auto tile = [&](auto par, int n) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    char* kn = P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2;    // K_n
     char* kn1 = P == 0 ? k_lds1 : P == 1 ? k_lds2 : k_lds0;   // K_{n+1}
     char* kn2 = P == 0 ? k_lds2 : P == 1 ? k_lds0 : k_lds1;   // receives K_{n+2}
     char* vn = P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2;    // V_n
@@ -315,18 +353,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     u32x4 pf[2][2];
     stage_rows(krs, kn2, tile_row(n + 2), voff, wave);
     stage_rows(vrs, vn1, tile_row(n + 1), voff, wave);
-    // half 0: scores of (n, 1) while exponentiating (n, 0)
-    W.scores(kn, 1, sn);
+    // half 0: scores of (n, 1) (operands from the previous step) while exponentiating (n, 0)
+    W.scores(ka, sn);
+    W.load_v(vn, 0, va);
+    W.load_k(kn1, 0, ka);
     if (__builtin_expect(!W.half_full(k0), 0)) W.mask(sc, k0);
-    W.decide(sc);
-    W.probs(sc, pf);
-    W.accumulate(vn, 0, pf);
+    W.softmax_half(sc, pf);
+    W.accumulate(va, pf);
     // half 1: scores of (n + 1, 0) while exponentiating (n, 1)
-    W.scores(kn1, 0, sc);
+    W.scores(ka, sc);
+    W.load_v(vn, 1, va);
+    W.load_k(kn1, 1, ka);
     if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.mask(sn, k0 + 32);
-    W.decide(sn);
-    W.probs(sn, pf);
-    W.accumulate(vn, 1, pf);
+    W.softmax_half(sn, pf);
+    W.accumulate(va, pf);
     lds_barrier<0>();  // this tile's loads have landed; its buffers are read no more
   };
   for (int n = 0; n < nt; n += 3) {
