@@ -71,7 +71,7 @@ int fill_bwd(const gqa_problem* p, BwdParams* bp) {
   bp->scale_log2 = p->scale * kLog2e;
   bp->mask = normalised_mask(p);
   row_decomposition(p, &bp->hpw, &bp->qpw, &bp->n_qblk);
-  bp->n_kblk = (p->S + 4 * gqa::kTile - 1) / (4 * gqa::kTile);
+  bp->n_kblk = (p->S + gqa::kDkdvKeys - 1) / gqa::kDkdvKeys;
   if (!grid_ok((long long)bp->n_qblk * p->B * (p->H / bp->hpw))) return GQA_ERR_UNSUPPORTED;
   if (!grid_ok((long long)bp->n_kblk * p->B * p->G)) return GQA_ERR_UNSUPPORTED;
   if (!grid_ok((long long)p->B * p->H * ((p->S + 63) / 64))) return GQA_ERR_UNSUPPORTED;

@@ -2,7 +2,8 @@
 // inputs, fp32 gradients).  Loss convention L = <O, dO>.
 //
 //   preprocess : delta_i = sum_c dO_ic O_ic                       (HBM-bound, fp32)
-//   dK/dV      : per (b, g, 256-key block), 8 waves x 32 keys (two waves per SIMD).  For
+//   dK/dV      : per (b, g, 128-key block), 4 waves x 32 keys (two workgroups, two waves
+//                per SIMD, per CU, so one's barrier waits are covered by the other).  For
 //                every query head of the group and every query tile that sees the block:
 //                  S  = Q K^T        P = exp(scale*S - lse)   (recomputed from the saved lse)
 //                  delta - dP = dO (-V)^T + delta  (V enters negated, the accumulator
@@ -227,8 +228,8 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
   const int rest = (int)(blockIdx.x % per_k);
   const int b = rest / p.G;
   const int g = rest % p.G;
-  const int K0 = kblk * 4 * kTile;
-  const int K1 = imin(K0 + 4 * kTile, S) - 1;
+  const int K0 = kblk * kDkdvKeys;
+  const int K1 = imin(K0 + kDkdvKeys, S) - 1;
 
   DkdvWave<DT> W;
   W.lane = lane;
@@ -255,11 +256,11 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
     W.dv[db] = f32x16{};
   }
 
-  // Staging by direct loads into LDS (no registers): wave w loads LDS rows 8w..8w+7 of the
+  // Staging by direct loads into LDS (no registers): wave w loads LDS rows 16w..16w+15 of the
   // Q and dO tiles; waves 0 and 1 load the lse and delta rows (a full 1 KiB load each, of
   // which the first 64 entries are the tile's).  Rows past the end of the sequence read
   // zero, which makes their P V and dS contributions vanish (Q and dO rows are zero).
-  const int voff = direct_voff(wave, lane);
+  const int voff0 = direct_voff(2 * wave, lane), voff1 = direct_voff(2 * wave + 1, lane);
   const TileRanges tr = query_tiles_for_keys(W.m, K0, K1);
   const int nq = tr.count();
   const int n_iter = nq * hpg;
@@ -269,8 +270,10 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
     const size_t slab = (size_t)(b * p.H + g * hpg + hh) * S;
     const __amdgpu_buffer_rsrc_t qr = slab_rsrc((const uint16_t*)p.q + slab * kHeadDim, S);
     const __amdgpu_buffer_rsrc_t dr = slab_rsrc((const uint16_t*)p.d_o + slab * kHeadDim, S);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(sb->q_rm + 1024 * wave), 16, qt * kTile * 128 + voff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 1024 * wave), 16, qt * kTile * 128 + voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(sb->q_rm + 2048 * wave), 16, qt * kTile * 128 + voff0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(sb->q_rm + 2048 * wave + 1024), 16, qt * kTile * 128 + voff1, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 2048 * wave), 16, qt * kTile * 128 + voff0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 2048 * wave + 1024), 16, qt * kTile * 128 + voff1, 0, 0, 0);
     if (wave < 2) {
       const float* base = (wave == 0 ? p.lse : p.delta) + slab;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, S * 4, 0x00020000);
@@ -329,12 +332,12 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   // Sink keys collect attention from every later query, so their dK and dV are sums of
   // many large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value
   // plus its rounded residual (two products each), which keeps their rounding out of the sum.
   const int kblk = (int)(blockIdx.x / (p.B * p.G));
-  if (p.mask.window > 0 && kblk * 4 * kTile < p.mask.sinks)
+  if (p.mask.window > 0 && kblk * kDkdvKeys < p.mask.sinks)
     dkdv_block<DT, true>(p);
   else
     dkdv_block<DT, false>(p);
@@ -552,7 +555,7 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s) {
-  dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(512);
+  dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(256);
   void* args[] = {(void*)&p};
   if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtBF16>, grid, block, args, 0, s);
   return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtF16>, grid, block, args, 0, s);

@@ -15,6 +15,7 @@
 namespace gqa {
 
 constexpr int kTile = 64;   // keys per key tile and query rows per wave tile
+constexpr int kDkdvKeys = 128;  // keys per dK/dV workgroup (4 waves x 32 keys)
 constexpr int kHeadDim = 64;
 
 enum TileClass : int { kEmpty = 0, kPartial = 1, kFull = 2 };
@@ -152,7 +153,7 @@ struct BwdParams {
   float scale_log2;
   MaskSpec mask;
   int hpw, qpw, n_qblk;  // dQ pass: same row decomposition as the forward
-  int n_kblk;            // dK/dV pass: 256-key blocks per kv head
+  int n_kblk;            // dK/dV pass: kDkdvKeys-key blocks per kv head
 };
 
 // Launchers (return hipSuccess or the launch error).  Element type by dtype code.
