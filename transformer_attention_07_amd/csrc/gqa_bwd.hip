@@ -15,9 +15,10 @@
 //                (double-buffered, one barrier per tile); the transposed operands dO^T
 //                and Q^T come from the row-major tiles through ds_read_b64_tr_b16.
 //   dQ         : per (b, h, 64-row tile), the forward's decomposition (two waves per
-//                SIMD).  For every key tile it sees: S^T = K Q^T, dP^T = V dO^T,
-//                dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.  K and V tiles arrive by
-//                direct loads into LDS.  Deterministic (each dQ element has one writer).
+//                SIMD).  For every key tile it sees: S^T = K Q^T, dP^T - delta = V dO^T +
+//                (-delta) (the accumulator starts at the lane's -delta), dS^T = P^T (dP^T -
+//                delta), dQ^T += K^T dS^T.  K and V tiles arrive by direct loads into LDS.
+//                Deterministic (each dQ element has one writer).
 //
 // Every staging buffer is its own LDS object and both loops are unrolled by two, so the
 // buffer a step reads is known at compile time to differ from the one the direct loads of
@@ -92,6 +93,15 @@ struct DkdvStage {
   float lse[256];    // lse of the tile's 64 rows (entries 64.. are load padding); 0 past the end
   float delta[256];  // delta, likewise
 };
+
+// classify() for wave-uniform bounds as one scalar value: bitwise terms, no branches.
+__device__ __forceinline__ int classify_uniform(const MaskSpec& m, int q0, int q1, int k0, int k1) {
+  const int c = m.causal != 0, w = m.window;
+  const int empty = (k0 >= m.S) | (c & (k0 > q1)) | (c & (w > 0) & (k1 <= q0 - w) & (k0 >= m.sinks));
+  const int full = ((c ^ 1) & (k1 < m.S)) |
+                   (c & (k1 <= q0) & (k1 < m.S) & ((w <= 0) | (k0 > q1 - w) | (k1 < m.sinks)));
+  return __builtin_amdgcn_readfirstlane(empty ? (int)kEmpty : full ? (int)kFull : (int)kPartial);
+}
 
 // The two staging buffers of the dK/dV pass, as distinct LDS objects so that the compiler
 // can tell the buffer being read from the one the direct loads are filling.
@@ -287,7 +297,7 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qr0 = qt * kTile + qb * 32;
-      const int cls = qr0 < S ? classify(W.m, qr0, imin(qr0 + 31, S - 1), W.kw0, W.kw1) : (int)kEmpty;
+      const int cls = classify_uniform(W.m, qr0, imin(qr0 + 31, S - 1), W.kw0, W.kw1);
       if (cls == kEmpty) continue;
       W.template block<PRECISE>(sb, qb, qr0, cls != kFull);
     }
@@ -412,6 +422,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     dlt[cb] = ok ? p.delta[qslab_rows + row] : 0.f;
   }
 
+  // -delta of the lane's query row, replicated over an accumulator: the initial value of
+  // dP^T, which then holds dP - delta (loop-invariant, so set up once)
+  f32x16 ndlt[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndlt[cb][r] = -dlt[cb];
+
   f32x16 dq[2][2];  // dQ^T [d block][column block]
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -449,10 +467,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         s[cb] = mfma32<DT>(ak, qf[cb][ks], ks == 0 ? f32x16{} : s[cb]);
-        dp[cb] = mfma32<DT>(av, df[cb][ks], ks == 0 ? f32x16{} : dp[cb]);
+        dp[cb] = mfma32<DT>(av, df[cb][ks], ks == 0 ? ndlt[cb] : dp[cb]);
       }
     }
-    if (__builtin_expect(!(kr0 + 31 <= lim_hi && (kr0 >= win_lo || kr0 + 31 < m.sinks)), 0)) {
+    const bool full = __builtin_amdgcn_readfirstlane((int)(kr0 + 31 <= lim_hi) &
+                                                     ((int)(kr0 >= win_lo) | (int)(kr0 + 31 < m.sinks))) != 0;
+    if (__builtin_expect(!full, 0)) {
       // lane = query column i, register r = key kr0 + 4*hl + rr(r)
       const int base = kr0 + 4 * hl;
       const int kmax = m.S - 1 - base;
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * t + e;
           const float pv = exp2_fast(__builtin_fmaf(s[cb][r], c2, -lse2[cb]));
-          dsv[e] = pv * (dp[cb][r] - dlt[cb]);
+          dsv[e] = pv * dp[cb][r];
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) pds[cb][t][w] = pack2<DT>(dsv[2 * w], dsv[2 * w + 1]);
