@@ -2,8 +2,9 @@
 """Benchmark of the fused causal grouped-query attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic inputs
-already resident in HBM: the forward (O, lse), then the backward (delta,
-dK/dV, dQ) for an upstream gradient dO.  The default workload is the causal
+already resident in HBM: the forward (O, lse), then the backward (delta, then
+dK/dV and dQ through gqa_attn_bwd_grads: one fused launch at the default
+workload) for an upstream gradient dO.  The default workload is the causal
 GQA shape B=4, H=32 query heads, G=8 kv heads, S=2048, d=64, bf16.
 
 Work is counted only on visible (query, key) pairs: forward 4*d*pairs*B*H flop
@@ -13,7 +14,7 @@ carries the step throughput, a roofline record for the dominant kernel (timed
 with HIP events on the stream the kernels run on) and the CPU fp64 oracle
 timed on a bounded sample of the same work on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50]
                        [--workload step|c2|c3|c4|c5] [--no-cpu-baseline]
 """
 
@@ -39,8 +40,10 @@ KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_device.h", "gqa_internal.h"
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU takes tens of milliseconds of sustained work to reach its steady clocks, so the
+    # defaults warm up for 50 steps before timing 100
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="step", choices=["step", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -88,7 +91,8 @@ def load_traffic(kernel, wname):
 
 
 KERNEL_KEYS = {"fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
-               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "copyBuffer": "copy"}
+               "bwd_fused_kernel": "bwd_grads", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq",
+               "copyBuffer": "copy"}
 COPY_BYTES = 1 << 30
 
 
@@ -208,7 +212,7 @@ def main():
     dv = torch.empty(kd.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    kernels = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq"] if do_bwd else [])
+    kernels = ["fwd"] + (["bwd_preprocess", "bwd_grads"] if do_bwd else [])
 
     def step(events=None):
         def mark(i):
@@ -220,10 +224,10 @@ def main():
         if do_bwd:
             gqa.gqa_attn_bwd_preprocess(o, dod, delta=delta, o_lo=o_lo, stream=stream)
             mark(2)
-            gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta, dk=dk, dv=dv, stream=stream, **kw)
+            # dK, dV and dQ: one fused launch when the dK/dV grid fits in one round of
+            # workgroup slots (the default workload), else the two passes back to back
+            gqa.gqa_attn_bwd_grads(qd, kd, vd, lse, dod, delta, dq=dq, dk=dk, dv=dv, stream=stream, **kw)
             mark(3)
-            gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta, dq=dq, stream=stream, **kw)
-            mark(4)
 
     for _ in range(args.warmup):
         step()
@@ -250,8 +254,7 @@ def main():
 
     pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
     bh = w.B * w.H
-    flop = {"fwd": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0, "bwd_dkdv": 8.0 * w.D * pairs * bh,
-            "bwd_dq": 2.0 * w.D * pairs * bh}
+    flop = {"fwd": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0, "bwd_grads": 10.0 * w.D * pairs * bh}
     elem = 2 if w.dtype in ("bf16", "f16") else 4
     hbm_bytes = {"bwd_preprocess": 3.0 * bh * w.S * w.D * elem + bh * w.S * 4}  # O, o_lo, dO in; delta out
     step_flop = flop["fwd"] + (10.0 * w.D * pairs * bh if do_bwd else 0.0)

@@ -112,8 +112,8 @@ size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p);
 /* Backward of L = <O, dO>: dQ, dK, dV (fp32, overwritten, not accumulated into) from the
  * forward's inputs, its output O (and optionally o_lo, see gqa_attn_fwd; NULL if not
  * kept) and its lse.  Runs gqa_attn_bwd_preprocess into the workspace, then
- * gqa_attn_bwd_dkdv and gqa_attn_bwd_dq, on one stream.  Deterministic: no
- * floating-point atomics, so repeated calls give bit-identical results. */
+ * gqa_attn_bwd_grads, on one stream.  Deterministic: no floating-point atomics, so
+ * repeated calls give bit-identical results. */
 int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v,
                  const void* o, const void* o_lo, const float* lse, const void* d_o, float* dq,
                  float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
@@ -133,6 +133,17 @@ int gqa_attn_bwd_dkdv(const gqa_problem* p, const void* q, const void* k, const 
 int gqa_attn_bwd_dq(const gqa_problem* p, const void* q, const void* k, const void* v,
                     const float* lse, const void* d_o, const float* delta, float* dq,
                     void* stream);
+
+/* Backward steps 2 and 3 together: dK, dV and dQ from delta, with results bit-identical to
+ * gqa_attn_bwd_dkdv followed by gqa_attn_bwd_dq.  For 16-bit inputs, when the dK/dV pass
+ * has no more workgroups than the device holds at once (two per compute unit), its work
+ * per workgroup is very uneven under a causal mask (the first key block sees every query,
+ * the last one almost none); then both passes go in one launch, so that dQ work fills the
+ * compute units the short key blocks leave idle.  Otherwise, and for GQA_F32, the two
+ * passes are launched one after the other.  Arguments and errors as for those two. */
+int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const void* v,
+                       const float* lse, const void* d_o, const float* delta, float* dq,
+                       float* dk, float* dv, void* stream);
 
 #ifdef __cplusplus
 }

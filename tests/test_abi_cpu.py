@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 9, declared
+    assert len(declared) == 10, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -103,6 +103,11 @@ def test_bwd_validation_and_workspace():
         == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_dq(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) \
         == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_grads(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) \
+        == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_grads(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, None) \
+        == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_grads(ctypes.byref(bad), *([FAKE] * 9), None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, None, None, FAKE, None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE + 2, FAKE, FAKE, None) == binding.GQA_ERR_INVALID_ARG
 

@@ -231,17 +231,28 @@ def test_backward_is_deterministic():
         assert torch.equal(a, b)
 
 
-def test_substeps_match_combined_backward():
-    w = Workload("sub", B=1, H=8, G=2, S=300, direction="fwd+bwd", seed=6)
+@pytest.mark.parametrize("shape", [dict(B=1, H=8, G=2, S=300, window=0, num_sinks=0),
+                                   dict(B=1, H=4, G=2, S=700, window=90, num_sinks=40),
+                                   dict(B=2, H=8, G=8, S=4608, window=0, num_sinks=0)],
+                         ids=["one-launch", "one-launch-window-sinks", "two-launches"])
+def test_substeps_match_combined_backward(shape):
+    # gqa_attn_bwd = preprocess + gqa_attn_bwd_grads; grads must equal dK/dV then dQ bit for
+    # bit, both where it fuses the passes into one launch (few dK/dV workgroups) and where
+    # it launches them separately (576 dK/dV workgroups, more than two per CU)
+    w = Workload("sub", direction="fwd+bwd", seed=6, **shape)
     q, k, v, do = make_inputs(w)
     (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
     dod = do.cuda()
-    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod)
+    kw = dict(causal=True, window=w.window, num_sinks=w.num_sinks)
+    print(f"[substeps] {shape}", flush=True)
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, dod, **kw)
     delta = gqa.gqa_attn_bwd_preprocess(o, dod)
-    dk2, dv2 = gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta)
-    dq2 = gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta)
+    dk2, dv2 = gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta, **kw)
+    dq2 = gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta, **kw)
+    dq3, dk3, dv3 = gqa.gqa_attn_bwd_grads(qd, kd, vd, lse, dod, delta, **kw)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dq3, dq2) and torch.equal(dk3, dk2) and torch.equal(dv3, dv2)
     # delta against its definition in fp64
     want = (o.double() * dod.double()).sum(-1)
     assert (delta.double() - want).abs().max().item() < 1e-4

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     gqa_attn_bwd,
     gqa_attn_bwd_dkdv,
     gqa_attn_bwd_dq,
+    gqa_attn_bwd_grads,
     gqa_attn_bwd_preprocess,
     gqa_attn_bwd_workspace_bytes,
     gqa_attn_fwd,

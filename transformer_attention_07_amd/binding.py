@@ -25,7 +25,7 @@ _DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_
 
 EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
-            "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq")
+            "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads")
 
 
 class GqaError(RuntimeError):
@@ -73,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_bwd_dkdv.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
     lib.gqa_attn_bwd_dq.restype = ctypes.c_int
     lib.gqa_attn_bwd_dq.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, vp]
+    lib.gqa_attn_bwd_grads.restype = ctypes.c_int
+    lib.gqa_attn_bwd_grads.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, fp, vp]
     _lib = lib
     return lib
 
@@ -250,6 +252,20 @@ def gqa_attn_bwd_dq(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks=0
     _check(library().gqa_attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
                                      _ptr(delta), _ptr(dq), _stream(stream)), "gqa_attn_bwd_dq")
     return dq
+
+
+def gqa_attn_bwd_grads(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks=0, scale=None, dq=None,
+                       dk=None, dv=None, stream=None):
+    """dQ, dK, dV from delta (steps 2 and 3 of the backward; one launch where that balances
+    the work better, identical results either way)."""
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q, k, v, q, lse, d_o)
+    _need(delta, "delta", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    dq, dk, dv = _grad_buffers(q, k, dq, dk, dv)
+    _check(library().gqa_attn_bwd_grads(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
+                                        _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "gqa_attn_bwd_grads")
+    return dq, dk, dv
 
 
 class GqaAttention(torch.autograd.Function):

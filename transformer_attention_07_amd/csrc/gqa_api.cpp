@@ -61,6 +61,18 @@ void row_decomposition(const gqa_problem* p, int* hpw, int* qpw, int* n_qblk) {
 
 int grid_ok(long long blocks) { return blocks > 0 && blocks <= INT_MAX; }
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+int current_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 int fill_bwd(const gqa_problem* p, BwdParams* bp) {
   *bp = BwdParams{};
   bp->B = p->B;
@@ -236,8 +248,40 @@ int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void*
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   float* delta = (float*)workspace;
   if ((rc = gqa_attn_bwd_preprocess(p, o, o_lo, d_o, delta, stream)) != GQA_OK) return rc;
-  if ((rc = gqa_attn_bwd_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, stream)) != GQA_OK) return rc;
-  return gqa_attn_bwd_dq(p, q, k, v, lse, d_o, delta, dq, stream);
+  return gqa_attn_bwd_grads(p, q, k, v, lse, d_o, delta, dq, dk, dv, stream);
+}
+
+int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
+                       const void* d_o, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  // When all dK/dV workgroups fit in one round of workgroup slots (two per CU), the causal
+  // spread of their work sets the pass's length; then dK/dV and dQ go in one launch and dQ
+  // workgroups fill the CUs that the short key blocks free.  Otherwise two launches.
+  const long long n_dkdv = (long long)bp.n_kblk * p->B * p->G;
+  const int cus = current_cu_count();
+  if (p->dtype == GQA_F32 || cus <= 0 || n_dkdv > 2LL * cus) {
+    if ((rc = gqa_attn_bwd_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, stream)) != GQA_OK) return rc;
+    return gqa_attn_bwd_dq(p, q, k, v, lse, d_o, delta, dq, stream);
+  }
+  if (!grid_ok(n_dkdv + (long long)bp.n_qblk * p->B * (p->H / bp.hpw))) return GQA_ERR_UNSUPPORTED;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  return hip_status(gqa::launch_bwd_fused_mfma(bp, p->dtype, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -224,7 +224,7 @@ __device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
 // key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
 // allocation instead of raising the common variant's.
 template <int DT, bool PRECISE>
-__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
+__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg) {
   const BwdParams p = uniform_params(pin);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -234,8 +234,8 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
 
   // heaviest (earliest) key blocks first
   const int per_k = p.B * p.G;
-  const int kblk = (int)(blockIdx.x / per_k);
-  const int rest = (int)(blockIdx.x % per_k);
+  const int kblk = wg / per_k;
+  const int rest = wg % per_k;
   const int b = rest / p.G;
   const int g = rest % p.G;
   const int K0 = kblk * kDkdvKeys;
@@ -341,16 +341,21 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin) {
     }
 }
 
+// Sink keys collect attention from every later query, so their dK and dV are sums of many
+// large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value plus
+// its rounded residual (two products each), which keeps their rounding out of the sum.
+template <int DT>
+__device__ __forceinline__ void dkdv_dispatch(const BwdParams& p, int wg) {
+  const int kblk = wg / (p.B * p.G);
+  if (p.mask.window > 0 && kblk * kDkdvKeys < p.mask.sinks)
+    dkdv_block<DT, true>(p, wg);
+  else
+    dkdv_block<DT, false>(p, wg);
+}
+
 template <int DT>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
-  // Sink keys collect attention from every later query, so their dK and dV are sums of
-  // many large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value
-  // plus its rounded residual (two products each), which keeps their rounding out of the sum.
-  const int kblk = (int)(blockIdx.x / (p.B * p.G));
-  if (p.mask.window > 0 && kblk * kDkdvKeys < p.mask.sinks)
-    dkdv_block<DT, true>(p);
-  else
-    dkdv_block<DT, false>(p);
+  dkdv_dispatch<DT>(p, (int)blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------------
@@ -363,7 +368,7 @@ __shared__ __attribute__((aligned(1024))) char g_dq_v0[8192];
 __shared__ __attribute__((aligned(1024))) char g_dq_v1[8192];
 
 template <int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, int wg) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int nhq = p.H / p.hpw;
   const int per_q = p.B * nhq;
-  const int qblk = p.n_qblk - 1 - (int)(blockIdx.x / per_q);
-  const int rest = (int)(blockIdx.x % per_q);
+  const int qblk = p.n_qblk - 1 - wg / per_q;
+  const int rest = wg % per_q;
   const int b = rest / nhq;
   const int h = (rest % nhq) * p.hpw + (wave % p.hpw);
   const int g = h / (p.H / p.G);
@@ -560,6 +565,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+  dq_body<DT>(p, (int)blockIdx.x);
+}
+
+template <int DT>
+__device__ __attribute__((noinline)) void dq_block(const BwdParams& pin, int wg) {
+  dq_body<DT>(uniform_params(pin), wg);
+}
+
+// dK/dV and dQ in one launch: the dK/dV workgroups (heaviest key blocks first) come first,
+// then the dQ workgroups (heaviest query blocks first), so dQ work fills the CUs that the
+// light dK/dV blocks free while the heavy ones still run.  The two passes are independent
+// (both only read Q, K, V, dO, lse, delta) and each keeps its own register allocation.
+template <int DT>
+__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdParams p) {
+  const int n_dkdv = p.n_kblk * p.B * p.G;
+  const int wg = (int)blockIdx.x;
+  if (wg < n_dkdv)
+    dkdv_dispatch<DT>(p, wg);
+  else
+    dq_block<DT>(p, wg - n_dkdv);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s) {
@@ -586,6 +615,14 @@ hipError_t launch_bwd_dq_mfma(const BwdParams& p, int dtype, hipStream_t s) {
   void* args[] = {(void*)&p};
   if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_dq_kernel<kDtBF16>, grid, block, args, 0, s);
   return hipLaunchKernel((const void*)bwd_dq_kernel<kDtF16>, grid, block, args, 0, s);
+}
+
+hipError_t launch_bwd_fused_mfma(const BwdParams& p, int dtype, hipStream_t s) {
+  const long long n = (long long)p.n_kblk * p.B * p.G + (long long)p.n_qblk * p.B * (p.H / p.hpw);
+  dim3 grid((unsigned)n), block(256);
+  void* args[] = {(void*)&p};
+  if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_fused_kernel<kDtBF16>, grid, block, args, 0, s);
+  return hipLaunchKernel((const void*)bwd_fused_kernel<kDtF16>, grid, block, args, 0, s);
 }
 
 }  // namespace gqa

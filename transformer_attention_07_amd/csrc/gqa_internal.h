@@ -162,6 +162,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_fused_mfma(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdParams& p, hipStream_t s);
 
