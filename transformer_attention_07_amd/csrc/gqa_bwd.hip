@@ -193,8 +193,8 @@ struct DkdvWave {
   }
 };
 
-// Wave-uniform copies of the parameters: the out-of-line pass receives them in vector
-// registers, and buffer descriptors built from non-uniform values turn every buffer load
+// Wave-uniform copies of the parameters (and of the workgroup index): the out-of-line pass
+// receives its arguments in vector registers, and buffer descriptors built from non-uniform values turn every buffer load
 // into a waterfall loop.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float uni(float x) {
@@ -224,8 +224,9 @@ __device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
 // key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
 // allocation instead of raising the common variant's.
 template <int DT, bool PRECISE>
-__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg) {
+__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg_in) {
   const BwdParams p = uniform_params(pin);
+  const int wg = uni(wg_in);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
 template <int DT>
 __device__ __attribute__((noinline)) void dq_block(const BwdParams& pin, int wg) {
-  dq_body<DT>(uniform_params(pin), wg);
+  dq_body<DT>(uniform_params(pin), uni(wg));
 }
 
 // dK/dV and dQ in one launch: the dK/dV workgroups (heaviest key blocks first) come first,
