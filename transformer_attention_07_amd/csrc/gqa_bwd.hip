@@ -90,8 +90,8 @@ __device__ __forceinline__ int direct_voff(int j, int lane) {
 struct DkdvStage {
   char q_rm[8192];   // Q tile, row-major (rows = queries)
   char do_rm[8192];  // dO tile, row-major
-  float lse[256];    // lse of the tile's 64 rows (entries 64.. are load padding); 0 past the end
-  float delta[256];  // delta, likewise
+  float lse[64];     // lse * log2(e) of the tile's 64 rows; 0 past the end
+  float delta[256];  // delta of the tile's 64 rows (entries 64.. are load padding); 0 past the end
 };
 
 // classify() for wave-uniform bounds as one scalar value: bitwise terms, no branches.
@@ -117,6 +117,35 @@ struct DkdvWave {
   float c2;
   u32x4 kf[4], vf[4];  // K and -V rows as B operands [contraction step]
   f32x16 dk[2], dv[2];  // transposed accumulators [d block]
+  int trb[2][2];        // this lane's byte offsets of the transposed reads [d block][row half]
+
+  // The transposed reads of block (qb, t) address rows qb*32 + 16t + lr (+ 8) of a row-major
+  // tile, lr = 4*(lane/32) + (lane%16)/4 < 8.  The swizzle depends on a row's low four bits
+  // only, which the tile offset qb*32 + 16t leaves alone, and the d block flips chunk bit 2,
+  // which the lane's own chunk bits (0..1) never touch: the lane part of every address is
+  // one of four values and the rest is a constant.
+  __device__ __forceinline__ void init_tr_offsets() {
+    const int lr = 4 * hl + ((lane & 15) >> 2);
+    const int lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = lr + 8 * hf;
+        trb[db][hf] = row * 128 + (((lc ^ swz(row)) ^ (4 * db)) << 4) + 8 * (lane & 1);
+      }
+  }
+  // lds_rm_transposed_operand(tile, db, qb, t, lane) from the offsets above
+  __device__ __forceinline__ u32x4 tr_operand(const char* tile, int db, int qb, int t) const {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* base = tile + (qb * 32 + 16 * t) * 128;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + trb[db][0]));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + trb[db][1]));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+  }
 
   // one 32-query block qb of the staged tile (rows qr0 ..): both products for dK and dV
   template <bool PRECISE>
@@ -131,7 +160,7 @@ struct DkdvWave {
       const f32x4 dv4 = *(const f32x4*)(sb.delta + qb * 32 + 8 * r4 + 4 * hl);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        L[4 * r4 + x] = lv[x] * kLog2e;
+        L[4 * r4 + x] = lv[x];
         nd[4 * r4 + x] = dv4[x];
       }
     }
@@ -181,8 +210,8 @@ struct DkdvWave {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const u32x4 ado_t = lds_rm_transposed_operand(sb.do_rm, db, qb, t, lane);
-        const u32x4 aq_t = lds_rm_transposed_operand(sb.q_rm, db, qb, t, lane);
+        const u32x4 ado_t = tr_operand(sb.do_rm, db, qb, t);
+        const u32x4 aq_t = tr_operand(sb.q_rm, db, qb, t);
         dv[db] = mfma32<DT>(ado_t, pp[t], dv[db]);
         dk[db] = mfma32<DT>(aq_t, pds[t], dk[db]);
         if (PRECISE) {
@@ -250,6 +279,7 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
   W.kw1 = imin(W.kw0 + 31, S - 1);
   W.m = p.mask;
   W.c2 = p.scale_log2;
+  W.init_tr_offsets();
   const bool active = W.kw0 < S;
 
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + (size_t)(b * p.G + g) * S * kHeadDim, S);
@@ -268,14 +298,16 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
   }
 
   // Staging by direct loads into LDS (no registers): wave w loads LDS rows 16w..16w+15 of the
-  // Q and dO tiles; waves 0 and 1 load the lse and delta rows (a full 1 KiB load each, of
-  // which the first 64 entries are the tile's).  Rows past the end of the sequence read
-  // zero, which makes their P V and dS contributions vanish (Q and dO rows are zero).
+  // Q and dO tiles; wave 1 loads the delta row (a full 1 KiB load, of which the first 64
+  // entries are the tile's).  Wave 0 loads the tile's 64 lse values into a register and,
+  // once they have arrived, stores them scaled by log2(e), so that the exponent of every
+  // score takes a single fma.  Rows past the end of the sequence read zero, which makes
+  // their P V and dS contributions vanish (Q and dO rows are zero).
   const int voff0 = direct_voff(2 * wave, lane), voff1 = direct_voff(2 * wave + 1, lane);
   const TileRanges tr = query_tiles_for_keys(W.m, K0, K1);
   const int nq = tr.count();
   const int n_iter = nq * hpg;
-  auto stage_dma = [&](DkdvStage* sb, int iter) __attribute__((always_inline)) {
+  auto stage_dma = [&](DkdvStage* sb, int iter) __attribute__((always_inline)) -> float {
     const int hh = iter / nq;
     const int qt = tr.tile(iter % nq);
     const size_t slab = (size_t)(b * p.H + g * hpg + hh) * S;
@@ -285,11 +317,21 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(sb->q_rm + 2048 * wave + 1024), 16, qt * kTile * 128 + voff1, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 2048 * wave), 16, qt * kTile * 128 + voff0, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void*)(sb->do_rm + 2048 * wave + 1024), 16, qt * kTile * 128 + voff1, 0, 0, 0);
-    if (wave < 2) {
-      const float* base = (wave == 0 ? p.lse : p.delta) + slab;
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, S * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(wave == 0 ? sb->lse : sb->delta), 16,
-                                               (qt * kTile + 4 * lane) * 4, 0, 0, 0);
+    float lv = 0.f;
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse + slab), 0, S * 4, 0x00020000);
+      lv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (qt * kTile + lane) * 4, 0, 0));
+    } else if (wave == 1) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.delta + slab), 0, S * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)sb->delta, 16, (qt * kTile + 4 * lane) * 4, 0, 0, 0);
+    }
+    return lv;
+  };
+  // after the wait for the loads: wave 0 stores the scaled lse
+  auto stage_lse = [&](DkdvStage* sb, float lv) __attribute__((always_inline)) {
+    if (wave == 0) {
+      asm volatile("" : "+v"(lv));  // keeps the scaling (and so the wait for the load) here
+      sb->lse[lane] = lv * kLog2e;
     }
   };
   auto compute = [&](const DkdvStage& sb, int iter) __attribute__((always_inline)) {
@@ -304,17 +346,25 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
     }
   };
 
-  if (n_iter > 0) stage_dma(&g_dkdv_stage0, 0);
+  float lv0 = 0.f;
+  if (n_iter > 0) lv0 = stage_dma(&g_dkdv_stage0, 0);
   __builtin_amdgcn_s_waitcnt(0);
+  if (n_iter > 0) stage_lse(&g_dkdv_stage0, lv0);
   __syncthreads();
   // unrolled by two so that every LDS buffer is known at compile time (the loads into the
   // other buffer then need no wait before this buffer's reads)
   auto iter_body = [&](auto par, int it) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    if (it + 1 < n_iter) stage_dma(P ? &g_dkdv_stage0 : &g_dkdv_stage1, it + 1);
+    DkdvStage* next = P ? &g_dkdv_stage0 : &g_dkdv_stage1;
+    const bool more = it + 1 < n_iter;
+    float lv = 0.f;
+    if (more) lv = stage_dma(next, it + 1);
     compute(P ? g_dkdv_stage1 : g_dkdv_stage0, it);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): next stage landed, reads done
+    if (more) stage_lse(next, lv);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the lse store is done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
