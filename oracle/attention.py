@@ -184,6 +184,59 @@ def backward_group(q, k, v, do, b: int, g: int, scale=None, causal=True, window=
     return dq, dk, dv
 
 
+def backward_rows(q, k, v, do, b: int, h: int, rows, scale=None, causal=True, window=0, num_sinks=0):
+    """dQ[b, h, rows, :] of L = <O, dO>, fp64.
+
+    The same formulas as ``backward_group`` for the given query rows only: a
+    row's dQ needs nothing but its own row of P and dP.
+    """
+    B, H, S, D = q.shape
+    G = k.shape[1]
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    g = int(kv_head(h, H, G))
+    rows = np.asarray(rows, dtype=np.int64)
+    kk, vv = _f64(k[b, g]), _f64(v[b, g])
+    dq = np.empty((rows.size, D))
+    for c0 in range(0, rows.size, _ROW_CHUNK):
+        r = rows[c0:c0 + _ROW_CHUNK]
+        P, _ = _softmax_rows(_scores(_f64(q[b, h, r]), kk, r, scale, causal, window, num_sinks))
+        dP = _f64(do[b, h, r]) @ vv.T
+        Dr = (P * dP).sum(axis=1, keepdims=True)
+        dq[c0:c0 + r.size] = scale * ((P * (dP - Dr)) @ kk)
+    return dq
+
+
+def backward_keys(q, k, v, do, b: int, g: int, keys, scale=None, causal=True, window=0, num_sinks=0):
+    """dK[b, g, keys, :] and dV[b, g, keys, :] of L = <O, dO>, fp64.
+
+    The same formulas as ``backward_group``, evaluated on the query rows (of
+    every head of the group) that see at least one of the given keys; each of
+    those rows is taken in full, since its P needs all of its visible keys.
+    """
+    B, H, S, D = q.shape
+    G = k.shape[1]
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    hpg = H // G
+    keys = np.asarray(keys, dtype=np.int64)
+    kk, vv = _f64(k[b, g]), _f64(v[b, g])
+    sees = visible(np.arange(S)[:, None], keys[None, :], causal, window, num_sinks).any(axis=1)
+    rows = np.nonzero(sees)[0]
+    dk = np.zeros((keys.size, D))
+    dv = np.zeros((keys.size, D))
+    for t in range(hpg):
+        h = g * hpg + t
+        for c0 in range(0, rows.size, _ROW_CHUNK):
+            r = rows[c0:c0 + _ROW_CHUNK]
+            qh, doh = _f64(q[b, h, r]), _f64(do[b, h, r])
+            P, _ = _softmax_rows(_scores(qh, kk, r, scale, causal, window, num_sinks))
+            dP = doh @ vv.T
+            Dr = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - Dr)
+            dv += P[:, keys].T @ doh
+            dk += scale * (dS[:, keys].T @ qh)
+    return dk, dv
+
+
 def backward(q, k, v, do, scale=None, causal=True, window=0, num_sinks=0):
     """dQ [B,H,S,D], dK [B,G,S,D], dV [B,G,S,D] of L = <O, dO>, fp64."""
     B, H, S, D = q.shape

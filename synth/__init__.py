@@ -9,6 +9,14 @@ for workload k (1..5); ``torch.randn`` in fp32 in the fixed order Q, K, V, dO;
 each tensor then cast (round to nearest even) to the workload dtype on the CPU.
 Shapes follow the model card's attention layout (128 query heads over 16 KV
 heads, head dimension 64) and the tiny gate program's grouping (H=4, G=2).
+
+The long-context workload (k = 6: the model card's window 65,536 and 2,048
+sinks at S = 204,800, B = 2) holds 3.4e9 elements per query-sized tensor, so it
+is drawn per slab instead: slab (tensor n, batch b, head h) -- n = 0..3 in the
+order Q, K, V, dO -- gets its own generator seeded with
+``seed * 1_000_003 + (n * 4096 + b) * 4096 + h`` and ``torch.randn`` of one
+[S, D] fp32 slab, cast to the dtype; slabs are independent, so they are drawn
+on a thread pool.
 """
 
 from __future__ import annotations
@@ -18,7 +26,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows", "sample_rows_c4"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows", "sample_rows_c4", "sample_rows_long"]
 
 
 @dataclass(frozen=True)
@@ -36,6 +44,7 @@ class Workload:
     direction: str = "fwd"       # "fwd", "bwd" or "fwd+bwd"
     seed: int = 0
     desc: str = ""
+    per_slab: bool = False       # draw each [S, D] slab from its own generator (see above)
 
     @property
     def torch_dtype(self):
@@ -60,6 +69,9 @@ WORKLOADS = {
                    direction="fwd", seed=1238, desc="sliding-window + sink causal GQA fwd"),
     "c5": Workload("c5", B=4, H=32, G=8, S=4096, dtype="bf16", direction="bwd", seed=1239,
                    desc="causal GQA bwd from saved logsumexp, fp32 gradients"),
+    "long": Workload("long", B=2, H=128, G=16, S=204800, dtype="bf16", window=65536, num_sinks=2048,
+                     direction="fwd+bwd", seed=1240, per_slab=True,
+                     desc="the model card's long-context setting: window 65,536, 2,048 sinks, S=204,800"),
 }
 
 
@@ -68,8 +80,11 @@ def make_inputs(w: Workload, with_do: bool | None = None, seed: int | None = Non
     the direction has no backward and ``with_do`` is not forced."""
     if with_do is None:
         with_do = "bwd" in w.direction
+    base = w.seed if seed is None else seed
+    if w.per_slab:
+        return _make_inputs_per_slab(w, with_do, base)
     gen = torch.Generator(device="cpu")
-    gen.manual_seed(w.seed if seed is None else seed)
+    gen.manual_seed(base)
     shapes = [(w.B, w.H, w.S, w.D), (w.B, w.G, w.S, w.D), (w.B, w.G, w.S, w.D), (w.B, w.H, w.S, w.D)]
     out = []
     for n, shp in enumerate(shapes):
@@ -78,6 +93,25 @@ def make_inputs(w: Workload, with_do: bool | None = None, seed: int | None = Non
             break
         t = torch.randn(shp, generator=gen, dtype=torch.float32)
         out.append(t.to(w.torch_dtype).contiguous())
+    return tuple(out)
+
+
+def _make_inputs_per_slab(w: Workload, with_do: bool, base: int):
+    from concurrent.futures import ThreadPoolExecutor
+    heads = [w.H, w.G, w.G, w.H]
+    out = [torch.empty((w.B, heads[n], w.S, w.D), dtype=w.torch_dtype) for n in range(4 if with_do else 3)]
+
+    def slab(job):
+        n, b, h = job
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(base * 1_000_003 + (n * 4096 + b) * 4096 + h)
+        out[n][b, h] = torch.randn((w.S, w.D), generator=gen, dtype=torch.float32).to(w.torch_dtype)
+
+    jobs = [(n, b, h) for n in range(len(out)) for b in range(w.B) for h in range(heads[n])]
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        list(ex.map(slab, jobs))
+    if not with_do:
+        out.append(None)
     return tuple(out)
 
 
@@ -112,4 +146,22 @@ def sample_rows_c4(w: Workload, n: int = 4096):
             if 0 <= i < w.S:
                 trip.add((0, h, i))
     trip = sorted(trip)
+    return np.array(trip, dtype=np.int64).reshape(-1, 3)
+
+
+def sample_rows_long(w: Workload, n: int = 512):
+    """Rows checked at the long-context workload: ``n`` seeded random (b, h, i)
+    triples plus rows at the sink, window and tile edges and at 2^17 (first and
+    last head of two neighbouring kv groups in both batches)."""
+    rng = np.random.default_rng(w.seed)
+    flat = rng.choice(w.B * w.H * w.S, size=n, replace=False)
+    trip = set(zip(*[a.tolist() for a in np.unravel_index(flat, (w.B, w.H, w.S))]))
+    W, NS = w.window, w.num_sinks
+    forced = [0, 1, 63, 64, NS - 1, NS, W - 1, W, W + NS - 1, W + NS, 131071, 131072, w.S - 64, w.S - 1]
+    for b in (0, w.B - 1):
+        for h in (0, 7, 8, w.H - 1):
+            for i in forced:
+                if 0 <= i < w.S:
+                    trip.add((b, h, i))
+    trip = sorted((int(b), int(h), int(i)) for b, h, i in trip)
     return np.array(trip, dtype=np.int64).reshape(-1, 3)

@@ -238,6 +238,33 @@ def check_torch_sdpa(impl):
         assert np.allclose(dv, v.grad.numpy(), rtol=0, atol=1e-10), tag
 
 
+def check_sampled_backward_vs_torch(impl):
+    """dQ of chosen query rows and dK/dV of chosen keys (the row/key-restricted
+    oracle entry points used on the largest shapes) against autograd through
+    PyTorch's attention, on the same small cases."""
+    rng = _rng(19)
+    for (B, H, G, S, D, causal, W, NS) in TORCH_CASES:
+        qn, kn, vn, don = (_rand(rng, B, H, S, D), _rand(rng, B, G, S, D), _rand(rng, B, G, S, D),
+                           _rand(rng, B, H, S, D))
+        q, k, v = (torch.tensor(x, requires_grad=True) for x in (qn, kn, vn))
+        mask = _range_mask(S, causal, W, NS)
+        scale = 1.0 / math.sqrt(D)
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale, enable_gqa=(H != G))
+        (o * torch.tensor(don)).sum().backward()
+        kw = dict(scale=scale, causal=causal, window=W, num_sinks=NS)
+        tag = (B, H, G, S, D, causal, W, NS)
+        b = B - 1
+        rows = np.array(sorted({0, S // 2, S - 1, min(3, S - 1)}))
+        keys = np.array(sorted({0, 1, S // 3, S - 2, S - 1}))
+        for h in range(H):
+            dq = impl.backward_rows(qn, kn, vn, don, b, h, rows, **kw)
+            assert np.allclose(dq, q.grad[b, h, rows].numpy(), rtol=0, atol=1e-10), (tag, h)
+        for g in range(G):
+            dk, dv = impl.backward_keys(qn, kn, vn, don, b, g, keys, **kw)
+            assert np.allclose(dk, k.grad[b, g, keys].numpy(), rtol=0, atol=1e-10), (tag, g)
+            assert np.allclose(dv, v.grad[b, g, keys].numpy(), rtol=0, atol=1e-10), (tag, g)
+
+
 # --------------------------------------------------------------------------
 # 5. Gradients: central differences of L = <O, dO>, and exact identities.
 # --------------------------------------------------------------------------
@@ -292,4 +319,4 @@ def check_grad_identities(impl):
 
 ALL_CHECKS = [check_worked_example, check_rows_sum_to_one, check_token0, check_gqa_grouping,
               check_k_zero_closed_form, check_special_cases, check_torch_sdpa, check_fd_gradients,
-              check_grad_identities]
+              check_grad_identities, check_sampled_backward_vs_torch]
