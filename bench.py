@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PFLOP/s dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal GQA attention TFLOP/s (fwd, bwd) at d=64 + % of MI355X bf16 MFMA peak"
-KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_device.h", "gqa_internal.h"]
+KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_device.h", "gqa_internal.h"]
 
 
 def parse_args():
@@ -45,7 +45,8 @@ def parse_args():
     # whose step takes seconds)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="step", choices=["step", "c2", "c3", "c4", "c5", "long"])
+    ap.add_argument("--workload", default="step",
+                    choices=["step", "c2", "c3", "c4", "c5", "long", "decode", "decode16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -93,7 +94,7 @@ def load_traffic(kernel, wname):
 
 KERNEL_KEYS = {"fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
                "bwd_fused_kernel": "bwd_grads", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq",
-               "copyBuffer": "copy"}
+               "decode_split_kernel": "decode", "decode_merge_kernel": "decode_merge", "copyBuffer": "copy"}
 COPY_BYTES = 1 << 30
 
 
@@ -195,6 +196,90 @@ def cpu_baseline(w, inputs, budget_s):
                       f"{'fwd+bwd' if 'bwd' in w.direction else 'fwd'}), {dt:.1f} s, fp64 numpy"}
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode call: every cache row visible to at least one of
+    the Sq rows, K and V, read once per kv head; Q read and O written once; lse written."""
+    W, NS, Skv, Sq = w.window, w.num_sinks, w.Skv, w.Sq
+    if W >= Skv:
+        W = 0
+    if W == 0 or NS >= Skv:
+        W, NS = 0, 0
+    lo = max(0, Skv - Sq - W + 1) if W else 0  # first window key of the oldest row
+    keys = (Skv - lo) + min(NS, lo)
+    elem = 2
+    return (w.B * w.G * keys * w.D * 2 * elem + 2 * w.B * w.H * w.Sq * w.D * elem
+            + w.B * w.H * w.Sq * 4)
+
+
+def run_decode(args, w):
+    import numpy as np
+    import torch
+
+    import transformer_attention_07_amd as gqa
+    from synth import make_decode_inputs
+
+    print(f"[bench] decode workload {w}", file=sys.stderr, flush=True)
+    q, k, v = make_decode_inputs(w)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, gqa.gqa_attn_decode_workspace_bytes(qd, kd, w.window, w.num_sinks)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        gqa.gqa_attn_decode(qd, kd, vd, window=w.window, num_sinks=w.num_sinks, scale=w.scale, out=o, lse=lse,
+                            workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_call = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    nbytes = decode_bytes(w)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    ach = nbytes / (ms_call * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "decode (split-KV pass + merge, one call)", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("decode", w.name)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.attention as ref
+        from threadpoolctl import threadpool_info
+
+        print("[bench] timing the CPU oracle on one sequence", file=sys.stderr, flush=True)
+        t1 = time.perf_counter()
+        ref.decode(q[:1], k[:1], v[:1], scale=w.scale, window=w.window, num_sinks=w.num_sinks)
+        dt = time.perf_counter() - t1
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": nbytes / w.B / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"batch element 0 of {w.B} (all {w.H} heads, {w.Sq} rows each), {dt:.1f} s, fp64 numpy"}
+    wl = (f"decode, B={w.B} H={w.H} G={w.G} Sq={w.Sq} Skv={w.Skv} d={w.D}"
+          + (f" window={w.window} sinks={w.num_sinks}" if w.window else "") + f", {w.dtype}")
+    line = {
+        "metric": "decode attention HBM throughput (algorithmic bytes / time)", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic N(0,1), seeded",
+        "config": {"workload": wl, "B": w.B, "H": w.H, "G": w.G, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
+                   "window": w.window, "num_sinks": w.num_sinks, "bytes_per_step": nbytes,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels": {"decode": {"ms": round(ms_call, 5), "gbs": round(ach, 1)}},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -209,6 +294,18 @@ def main():
         args.steps = 3 if long_step else 100
     if args.warmup is None:
         args.warmup = 1 if long_step else 50
+    if args.workload.startswith("decode"):
+        import torch
+
+        import transformer_attention_07_amd as gqa
+        from synth import DECODE_WORKLOADS
+
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        gqa.library()
+        run_decode(args, DECODE_WORKLOADS[args.workload])
+        return
 
     import torch
 

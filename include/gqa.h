@@ -145,6 +145,52 @@ int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const
                        const float* lse, const void* d_o, const float* delta, float* dq,
                        float* dk, float* dv, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Decode: a few new query rows per head against a long key/value cache.
+ *
+ * The same operation as the forward, for the last Sq positions of a sequence of Skv keys:
+ * query row t of head h sits at position i = Skv - Sq + t and sees key j iff
+ *     j <= i  and  (window == 0  or  j > i - window  or  j < num_sinks)
+ * (always causal).  This is generation with a key/value cache: the model card's inference
+ * call flash_attention_fwd(Q, K, V, causal=True, sliding_window=..., num_sinks=...) with the
+ * cache as K and V and only the newest tokens as Q ("SnapKitty Transformer 8B" model card:
+ * FlashAttention Inference and Text Generation examples, and the KV Cache column of its
+ * Memory Usage table).
+ *
+ * Layout (dense, row-major):
+ *     Q, O   [B][H][Sq][D]    element type from dtype (GQA_BF16 or GQA_F16)
+ *     K, V   [B][G][Skv][D]   the cache, same element type
+ *     lse    [B][H][Sq]       fp32, natural log of the scaled scores
+ * The key range is split across workgroups (split-KV): each writes a partial softmax state
+ * (unnormalised O, running maximum, row sum) to the workspace, and a second kernel merges
+ * the partials of every row with the log-sum-exp rule.  The split depends only on the
+ * problem and the device's compute-unit count, so results are deterministic on a device. */
+typedef struct gqa_decode_problem {
+  int32_t B;         /* batch                                                          */
+  int32_t H;         /* query heads; H % G == 0                                        */
+  int32_t G;         /* key/value heads                                                */
+  int32_t Sq;        /* query rows per head, 1 <= Sq <= Skv (0 with B == 0: empty)     */
+  int32_t Skv;       /* keys in the cache                                              */
+  int32_t D;         /* head dimension (64)                                            */
+  float scale;       /* softmax scale applied to q.k; finite and > 0                   */
+  int32_t window;    /* 0: no window; W > 0: also require j > i - W (unless a sink)     */
+  int32_t num_sinks; /* keys j < num_sinks ignore the window (still causal); >= 0      */
+  int32_t dtype;     /* gqa_dtype of Q, K, V and O: GQA_BF16 or GQA_F16                */
+} gqa_decode_problem;
+
+/* Bytes of device workspace gqa_attn_decode needs on the current device (the partial
+ * softmax states of every split), rounded up to 256; 0 for an invalid or empty problem. */
+size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p);
+
+/* Decode attention.  Reads Q, K, V; writes O (dtype) and lse (fp32).  The workspace (device
+ * memory, at least gqa_attn_decode_workspace_bytes, 16-byte aligned) is scratch owned by the
+ * caller; its contents need no initialisation and are meaningless afterwards.  Errors:
+ * GQA_ERR_INVALID_ARG for bad sizes, pointers or alignment (Sq > Skv included),
+ * GQA_ERR_UNSUPPORTED for D != 64 or GQA_F32, GQA_ERR_WORKSPACE for a missing or short
+ * workspace, GQA_ERR_HIP if a launch fails.  B == 0 returns GQA_OK without a launch. */
+int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, const void* v,
+                    void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

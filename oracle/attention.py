@@ -252,6 +252,29 @@ def backward(q, k, v, do, scale=None, causal=True, window=0, num_sinks=0):
     return dq, dk, dv
 
 
+def decode(q, k, v, scale=None, window=0, num_sinks=0):
+    """Decode against a key/value cache: q [B,H,Sq,D] holds the newest Sq positions
+    Skv - Sq .. Skv - 1 of a sequence whose keys and values are k, v [B,G,Skv,D]
+    (the cache).  The same causal, windowed, sink-keeping attention as ``forward``
+    for those rows; returns O [B,H,Sq,D] and lse [B,H,Sq], fp64.  (The model card's
+    inference call over a cache: FlashAttention Inference and Text Generation
+    examples, KV Cache column of the Memory Usage table.)
+    """
+    B, H, Sq, D = q.shape
+    G, Skv = k.shape[1], k.shape[2]
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    positions = np.arange(Skv - Sq, Skv, dtype=np.int64)
+    out = np.empty((B, H, Sq, D))
+    lse = np.empty((B, H, Sq))
+    for b in range(B):
+        for h in range(H):
+            g = int(kv_head(h, H, G))
+            kk, vv = _f64(k[b, g]), _f64(v[b, g])
+            P, lse[b, h] = _softmax_rows(_scores(_f64(q[b, h]), kk, positions, scale, True, window, num_sinks))
+            out[b, h] = P @ vv
+    return out, lse
+
+
 def visible_pairs_per_head(S: int, causal=True, window=0, num_sinks=0) -> int:
     """Number of visible (i, j) pairs of one head, counted row by row."""
     total = 0

@@ -26,7 +26,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows", "sample_rows_c4", "sample_rows_long"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows", "sample_rows_c4", "sample_rows_long",
+           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -165,3 +166,49 @@ def sample_rows_long(w: Workload, n: int = 512):
                     trip.add((b, h, i))
     trip = sorted((int(b), int(h), int(i)) for b, h, i in trip)
     return np.array(trip, dtype=np.int64).reshape(-1, 3)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode against a key/value cache: Sq query rows per head at the newest positions of
+    Skv keys.  Inputs: the same recipe as above (one seeded generator, fp32 normals in the
+    order Q [B,H,Sq,D], K [B,G,Skv,D], V [B,G,Skv,D], each cast to the dtype)."""
+    name: str
+    B: int
+    H: int
+    G: int
+    Sq: int
+    Skv: int
+    D: int = 64
+    dtype: str = "bf16"
+    window: int = 0
+    num_sinks: int = 0
+    seed: int = 0
+    desc: str = ""
+
+    @property
+    def torch_dtype(self):
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+DECODE_WORKLOADS = {
+    # one new token per sequence, four sequences, the card's head layout, window and sinks
+    "decode": DecodeWorkload("decode", B=4, H=128, G=16, Sq=1, Skv=131072, window=65536, num_sinks=2048,
+                             seed=1241, desc="decode of one token against a 131,072-key cache"),
+    # sixteen new tokens (speculative / chunked decode) at the card's longest sequence
+    "decode16": DecodeWorkload("decode16", B=1, H=128, G=16, Sq=16, Skv=204800, window=65536,
+                               num_sinks=2048, seed=1242, desc="16 query rows against a 204,800-key cache"),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int | None = None):
+    """CPU tensors (q, k, v) in the workload dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    shapes = [(w.B, w.H, w.Sq, w.D), (w.B, w.G, w.Skv, w.D), (w.B, w.G, w.Skv, w.D)]
+    return tuple(torch.randn(shp, generator=gen, dtype=torch.float32).to(w.torch_dtype).contiguous()
+                 for shp in shapes)

@@ -266,6 +266,51 @@ def check_sampled_backward_vs_torch(impl):
 
 
 # --------------------------------------------------------------------------
+# 4b. Decode against a cache: the newest Sq positions of a sequence of Skv keys.
+# --------------------------------------------------------------------------
+DECODE_CASES = [(1, 4, 2, 1, 1, 4, 0, 0), (2, 4, 2, 1, 37, 5, 0, 0), (1, 8, 2, 3, 40, 6, 7, 3),
+                (1, 6, 3, 5, 21, 4, 4, 6), (2, 4, 4, 2, 17, 3, 0, 0), (1, 2, 1, 16, 64, 8, 16, 4),
+                (1, 4, 1, 9, 9, 3, 0, 0)]
+
+
+def check_decode_vs_torch(impl):
+    rng = _rng(20)
+    for (B, H, G, Sq, Skv, D, W, NS) in DECODE_CASES:
+        q, k, v = _rand(rng, B, H, Sq, D), _rand(rng, B, G, Skv, D), _rand(rng, B, G, Skv, D)
+        mask = _range_mask(Skv, True, W, NS)[Skv - Sq:]  # rows of the newest Sq positions
+        scale = 1.0 / math.sqrt(D)
+        qt, kt, vt = (torch.tensor(x) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=(H != G))
+        sc = scale * (qt @ kt.repeat_interleave(H // G, dim=1).transpose(-1, -2))
+        lse_t = torch.logsumexp(sc.masked_fill(~mask, float("-inf")), dim=-1)
+        O, lse = impl.decode(q, k, v, scale=scale, window=W, num_sinks=NS)
+        tag = (B, H, G, Sq, Skv, D, W, NS)
+        assert np.allclose(O, o.numpy(), rtol=0, atol=1e-11), tag
+        assert np.allclose(lse, lse_t.numpy(), rtol=0, atol=1e-11), tag
+
+
+def check_decode_k_zero_closed_form(impl):
+    # K = 0: every visible key has score 0, so each row is the plain mean of the V rows it
+    # sees and lse = ln(number of them); row t sits at position Skv - Sq + t
+    rng = _rng(21)
+    for Skv, W, NS in K0_CASES:
+        for Sq in sorted({1, min(4, Skv), Skv}):
+            B, H, G, D = 1, 4, 2, 3
+            q, v = _rand(rng, B, H, Sq, D), _rand(rng, B, G, Skv, D)
+            k = np.zeros((B, G, Skv, D))
+            O, lse = impl.decode(q, k, v, window=W, num_sinks=NS)
+            for g in range(G):
+                csum = np.concatenate([np.zeros((1, D)), np.cumsum(v[0, g], axis=0)])
+                for t in range(Sq):
+                    rs = visible_ranges(Skv - Sq + t, W, NS)
+                    n = sum(hi - lo for lo, hi in rs)
+                    mean = sum(csum[hi] - csum[lo] for lo, hi in rs) / n
+                    for h in range(g * (H // G), (g + 1) * (H // G)):
+                        assert abs(lse[0, h, t] - math.log(n)) < 1e-12, (Skv, W, NS, Sq, t)
+                        assert np.allclose(O[0, h, t], mean, rtol=0, atol=1e-12), (Skv, W, NS, Sq, t)
+
+
+# --------------------------------------------------------------------------
 # 5. Gradients: central differences of L = <O, dO>, and exact identities.
 # --------------------------------------------------------------------------
 FD_CASES = [(1, 4, 2, 6, 3, True, 0, 0), (1, 4, 2, 7, 3, True, 3, 2), (2, 2, 1, 5, 2, False, 0, 0),
@@ -319,4 +364,5 @@ def check_grad_identities(impl):
 
 ALL_CHECKS = [check_worked_example, check_rows_sum_to_one, check_token0, check_gqa_grouping,
               check_k_zero_closed_form, check_special_cases, check_torch_sdpa, check_fd_gradients,
-              check_grad_identities, check_sampled_backward_vs_torch]
+              check_grad_identities, check_sampled_backward_vs_torch, check_decode_vs_torch,
+              check_decode_k_zero_closed_form]

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 12, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -110,6 +110,54 @@ def test_bwd_validation_and_workspace():
     assert lib.gqa_attn_bwd_grads(ctypes.byref(bad), *([FAKE] * 9), None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, None, None, FAKE, None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE + 2, FAKE, FAKE, None) == binding.GQA_ERR_INVALID_ARG
+
+
+def _dec(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return gqa.library().gqa_attn_decode(ctypes.byref(p), q, k, v, o, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=6, G=4), binding.GQA_ERR_INVALID_ARG),          # H % G != 0
+    (dict(G=0), binding.GQA_ERR_INVALID_ARG),
+    (dict(B=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(Sq=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(Skv=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(Sq=9, Skv=8), binding.GQA_ERR_INVALID_ARG),      # the rows are positions of the cache
+    (dict(scale=0.0), binding.GQA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.GQA_ERR_INVALID_ARG),
+    (dict(window=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(num_sinks=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(dtype=7), binding.GQA_ERR_INVALID_ARG),
+    (dict(dtype=binding.GQA_F32), binding.GQA_ERR_UNSUPPORTED),
+    (dict(D=128), binding.GQA_ERR_UNSUPPORTED),
+    (dict(Skv=(1 << 24) + 1), binding.GQA_ERR_UNSUPPORTED),
+])
+def test_decode_validation(kw, status):
+    args = dict(B=1, H=8, G=2, Sq=1, Skv=4096, D=64, scale=0.125, window=0, num_sinks=0, dtype=binding.GQA_BF16)
+    args.update(kw)
+    p = binding.gqa_decode_problem(**args)
+    assert _dec(p) == status
+    assert gqa.library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_decode_pointers_workspace_and_empty():
+    lib = gqa.library()
+    p = gqa.make_decode_problem(2, 8, 2, 3, 1000, window=256, num_sinks=16)
+    need = lib.gqa_attn_decode_workspace_bytes(ctypes.byref(p))
+    # one partial state per split and wave: O (128 x 64 fp32) plus maximum and sum (2 x 128)
+    per_part = 128 * 64 * 4 + 2 * 128 * 4
+    assert need > 0 and need % 256 == 0 and need % per_part == 0
+    assert _dec(p, q=None) == binding.GQA_ERR_INVALID_ARG
+    assert _dec(p, lse=None) == binding.GQA_ERR_INVALID_ARG
+    assert _dec(p, k=FAKE + 2) == binding.GQA_ERR_INVALID_ARG
+    assert _dec(p, o=FAKE + 8) == binding.GQA_ERR_INVALID_ARG
+    assert _dec(p, ws=FAKE + 4) == binding.GQA_ERR_INVALID_ARG
+    assert _dec(p, ws=None, ws_bytes=need) == binding.GQA_ERR_WORKSPACE
+    assert _dec(p, ws_bytes=need - 1) == binding.GQA_ERR_WORKSPACE
+    for B, Sq in [(0, 1), (2, 0)]:
+        e = gqa.make_decode_problem(B, 8, 2, Sq, 100)
+        assert _dec(e, None, None, None, None, None, None, 0) == binding.GQA_OK
+        assert lib.gqa_attn_decode_workspace_bytes(ctypes.byref(e)) == 0
 
 
 @pytest.mark.parametrize("S,causal,W,NS", [(1, True, 0, 0), (50, True, 0, 0), (50, False, 0, 0), (50, True, 7, 0),

@@ -19,10 +19,14 @@ from .binding import (  # noqa: F401
     gqa_attn_bwd_grads,
     gqa_attn_bwd_preprocess,
     gqa_attn_bwd_workspace_bytes,
+    gqa_attn_decode,
+    gqa_attn_decode_workspace_bytes,
     gqa_attn_fwd,
+    gqa_decode_problem,
     gqa_problem,
     gqa_visible_pairs,
     library,
+    make_decode_problem,
     make_problem,
     status_str,
 )

@@ -25,7 +25,8 @@ _DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_
 
 EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
-            "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads")
+            "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads",
+            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode")
 
 
 class GqaError(RuntimeError):
@@ -39,6 +40,13 @@ class gqa_problem(ctypes.Structure):
                 ("S", ctypes.c_int32), ("D", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("num_sinks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class gqa_decode_problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -75,6 +83,11 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_bwd_dq.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, vp]
     lib.gqa_attn_bwd_grads.restype = ctypes.c_int
     lib.gqa_attn_bwd_grads.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, fp, vp]
+    DP = ctypes.POINTER(gqa_decode_problem)
+    lib.gqa_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_attn_decode_workspace_bytes.argtypes = [DP]
+    lib.gqa_attn_decode.restype = ctypes.c_int
+    lib.gqa_attn_decode.argtypes = [DP, vp, vp, vp, vp, fp, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -295,3 +308,51 @@ def gqa_attention(q, k, v, causal=True, sliding_window=0, num_sinks=0, scale=Non
     sliding_window=..., num_sinks=...)`` maps to ``gqa_attention(q, k, v, ...)``.  The
     gradient with respect to lse is not propagated."""
     return GqaAttention.apply(q, k, v, causal, sliding_window, num_sinks, scale)
+
+
+def make_decode_problem(B, H, G, Sq, Skv, D=64, scale=None, window=0, num_sinks=0,
+                        dtype=torch.bfloat16) -> gqa_decode_problem:
+    code = dtype if isinstance(dtype, int) else _DTYPES.get(dtype, -1)
+    return gqa_decode_problem(int(B), int(H), int(G), int(Sq), int(Skv), int(D),
+                              float(1.0 / math.sqrt(D) if scale is None else scale),
+                              int(window), int(num_sinks), int(code))
+
+
+def _decode_problem_from(q, k, window, num_sinks, scale) -> gqa_decode_problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,H,Sq,D] and k/v [B,G,Skv,D]")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return make_decode_problem(B, H, k.shape[1], Sq, k.shape[2], D, scale, window, num_sinks, q.dtype)
+
+
+def gqa_attn_decode_workspace_bytes(q, k, window=0, num_sinks=0, scale=None) -> int:
+    p = _decode_problem_from(q, k, window, num_sinks, scale)
+    return int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def gqa_attn_decode(q, k, v, window=0, num_sinks=0, scale=None, out=None, lse=None, workspace=None,
+                    stream=None):
+    """Decode attention: the Sq query rows of q [B,H,Sq,D] are the newest positions
+    (Skv - Sq + t) of the cache k, v [B,G,Skv,D]; returns (O [B,H,Sq,D], lse [B,H,Sq] fp32)."""
+    p = _decode_problem_from(q, k, window, num_sinks, scale)
+    _need(q, "q", device=q.device)
+    _need(k, "k", dtype=q.dtype, device=q.device)
+    _need(v, "v", dtype=q.dtype, shape=k.shape, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _need(out, "out", dtype=q.dtype, shape=q.shape, device=q.device)
+    _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    nbytes = int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(library().gqa_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), ws_bytes, _stream(stream)), "gqa_attn_decode")
+    return out, lse

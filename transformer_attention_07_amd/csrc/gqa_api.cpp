@@ -92,6 +92,62 @@ int fill_bwd(const gqa_problem* p, BwdParams* bp) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
+
+// ---- decode ----
+int check_decode(const gqa_decode_problem* p) {
+  if (p == nullptr) return GQA_ERR_INVALID_ARG;
+  if (p->B < 0 || p->Sq < 0 || p->Skv < 0 || p->H < 1 || p->G < 1 || p->D < 1) return GQA_ERR_INVALID_ARG;
+  if (p->H % p->G != 0) return GQA_ERR_INVALID_ARG;
+  if (!(isfinite(p->scale) && p->scale > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (p->window < 0 || p->num_sinks < 0) return GQA_ERR_INVALID_ARG;
+  if (p->dtype != GQA_F32 && p->dtype != GQA_BF16 && p->dtype != GQA_F16) return GQA_ERR_INVALID_ARG;
+  if (p->Sq > p->Skv) return GQA_ERR_INVALID_ARG;  // the rows are the newest Sq positions of the cache
+  if (p->D != gqa::kHeadDim || p->dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
+  // in-slab byte offsets of the cache (Skv * 128) and the row count stay in 32 bits
+  if (p->Skv > (1 << 24) || (long long)p->B * p->H * p->Sq > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+bool empty_decode(const gqa_decode_problem* p) { return p->B == 0 || p->Sq == 0; }
+
+// Split plan shared by the workspace query and the launch: rows per (b, g) in chunks of
+// 128, the visible key tiles of the newest Sq positions, and enough splits per chunk to
+// give every compute unit a workgroup (one per CU: 128 KiB of LDS each), but no split with
+// fewer than 8 tiles (two per wave).  Workspace: per chunk and partial, O (128 x 64 fp32)
+// plus maximum and sum (2 x 128 fp32).
+int plan_decode(const gqa_decode_problem* p, gqa::DecodeParams* dp, size_t* ws_bytes) {
+  using gqa::kDecodeRows;
+  using gqa::kDecodeWaves;
+  *dp = gqa::DecodeParams{};
+  dp->B = p->B;
+  dp->H = p->H;
+  dp->G = p->G;
+  dp->Sq = p->Sq;
+  dp->Skv = p->Skv;
+  dp->hpg = p->H / p->G;
+  const long long rows = (long long)dp->hpg * p->Sq;
+  if (rows > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  dp->rows = (int)rows;
+  dp->nrc = (int)((rows + kDecodeRows - 1) / kDecodeRows);
+  dp->scale_log2 = p->scale * kLog2e;
+  gqa_problem q{p->B, p->H, p->G, p->Skv, p->D, p->scale, 1, p->window, p->num_sinks, p->dtype};
+  dp->mask = normalised_mask(&q);
+  dp->tiles = gqa::key_tiles_for_rows(dp->mask, p->Skv - p->Sq, p->Skv - 1);
+  const int nt = dp->tiles.count();
+  const long long sets = (long long)p->B * p->G * dp->nrc;
+  const int cus = current_cu_count();
+  long long nsplit = cus > 0 ? (cus + sets - 1) / sets : 1;
+  const long long cap = nt / 8 > 1 ? nt / 8 : 1;
+  if (nsplit > cap) nsplit = cap;
+  if (nsplit < 1) nsplit = 1;
+  dp->nsplit = (int)nsplit;
+  if (!grid_ok(sets * nsplit) || !grid_ok(((long long)p->B * p->H * p->Sq + 3) / 4)) return GQA_ERR_UNSUPPORTED;
+  const size_t parts = (size_t)sets * nsplit * kDecodeWaves;
+  const size_t bytes = parts * ((size_t)kDecodeRows * gqa::kHeadDim + 2 * kDecodeRows) * sizeof(float);
+  *ws_bytes = (bytes + 255) & ~(size_t)255;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +338,37 @@ int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const
   bp.dk = dk;
   bp.dv = dv;
   return hip_status(gqa::launch_bwd_fused_mfma(bp, p->dtype, (hipStream_t)stream));
+}
+
+size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p) {
+  if (check_decode(p) != GQA_OK || empty_decode(p)) return 0;
+  gqa::DecodeParams dp;
+  size_t bytes = 0;
+  if (plan_decode(p, &dp, &bytes) != GQA_OK) return 0;
+  return bytes;
+}
+
+int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_decode(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_decode(p)) return GQA_OK;
+  if (!q || !k || !v || !o || !lse) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+    return GQA_ERR_INVALID_ARG;
+  gqa::DecodeParams dp;
+  size_t need = 0;
+  if ((rc = plan_decode(p, &dp, &need)) != GQA_OK) return rc;
+  if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  dp.q = q;
+  dp.k = k;
+  dp.v = v;
+  dp.o = o;
+  dp.lse = lse;
+  const size_t parts = (size_t)p->B * p->G * dp.nrc * dp.nsplit * gqa::kDecodeWaves;
+  dp.part_o = (float*)workspace;
+  dp.part_ml = dp.part_o + parts * gqa::kDecodeRows * gqa::kHeadDim;
+  return hip_status(gqa::launch_decode(dp, p->dtype, (hipStream_t)stream));
 }
 
 }  // extern "C"

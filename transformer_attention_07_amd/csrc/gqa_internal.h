@@ -157,6 +157,34 @@ struct BwdParams {
 };
 
 // Launchers (return hipSuccess or the launch error).  Element type by dtype code.
+// Decode (few query rows against a key/value cache), split over the visible key tiles.
+// Rows of a (batch, kv head) pair: r = hh * Sq + t for query head g * hpg + hh and query
+// row t (position Skv - Sq + t), in chunks of kDecodeRows; every wave of the split kernel
+// is one partial over its own key tiles and writes its unnormalised O, running maximum
+// (log2 units of the scaled score) and row sum, which the merge kernel combines.
+constexpr int kDecodeRows = 128;  // rows per chunk (four 32-row MFMA column blocks)
+constexpr int kDecodeWaves = 4;   // waves (= partials) per workgroup
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;     // [n_sets][n_part][kDecodeRows][64]
+  float* part_ml;    // [n_sets][n_part][2][kDecodeRows]: maximum, row sum
+  int B, H, G, Sq, Skv;
+  int hpg;           // H / G
+  int rows;          // hpg * Sq
+  int nrc;           // row chunks per (b, g) = ceil(rows / kDecodeRows)
+  int nsplit;        // workgroups per (b, g, chunk); partials per set = 4 * nsplit
+  float scale_log2;  // scale * log2(e)
+  MaskSpec mask;     // S = Skv, causal
+  TileRanges tiles;  // key tiles visible to at least one row (sinks, then window)
+};
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
+
 hipError_t launch_fwd_mfma(const FwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s);
