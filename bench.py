@@ -235,6 +235,10 @@ def run_decode(args, w):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    if args.copy_calibration:  # a plain copy of known size, for counter calibration
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
@@ -287,7 +291,8 @@ def main():
               "single MI355X (no collectives, no sharding); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.reduce_counters:
-        reduce_counters(*args.reduce_counters, workload(args.workload).name)
+        reduce_counters(*args.reduce_counters,
+                        args.workload if args.workload.startswith("decode") else workload(args.workload).name)
         return
     long_step = args.workload == "long"
     if args.steps is None:

@@ -291,9 +291,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int n_part = p.nsplit * kDecodeWaves;
   const float* ml = p.part_ml + (size_t)set * n_part * 2 * kDecodeRows + rr;
   const float* po = p.part_o + ((size_t)set * n_part * kDecodeRows + rr) * kHeadDim + lane;
+  // unrolled so that the partials' loads are in flight together
   float mstar = -INFINITY;
+#pragma unroll 8
   for (int i = 0; i < n_part; ++i) mstar = vmax(mstar, ml[(size_t)i * 2 * kDecodeRows]);
   float L = 0.f, acc = 0.f;
+#pragma unroll 8
   for (int i = 0; i < n_part; ++i) {
     const float mi = ml[(size_t)i * 2 * kDecodeRows];
     const float w = mi == -INFINITY ? 0.f : exp2_fast(mi - mstar);
