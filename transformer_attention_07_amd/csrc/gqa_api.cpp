@@ -112,8 +112,7 @@ bool empty_decode(const gqa_decode_problem* p) { return p->B == 0 || p->Sq == 0;
 
 // Split plan shared by the workspace query and the launch: rows per (b, g) in chunks of
 // 128, the visible key tiles of the newest Sq positions, and enough splits per chunk to
-// give every compute unit a workgroup (one per CU: 128 KiB of LDS each), but no split with
-// fewer than 8 tiles (two per wave).  Workspace: per chunk and partial, O (128 x 64 fp32)
+// fill every compute unit (see below).  Workspace: per chunk and partial, O (128 x 64 fp32)
 // plus maximum and sum (2 x 128 fp32).
 int plan_decode(const gqa_decode_problem* p, gqa::DecodeParams* dp, size_t* ws_bytes) {
   using gqa::kDecodeRows;
@@ -135,14 +134,22 @@ int plan_decode(const gqa_decode_problem* p, gqa::DecodeParams* dp, size_t* ws_b
   dp->tiles = gqa::key_tiles_for_rows(dp->mask, p->Skv - p->Sq, p->Skv - 1);
   const int nt = dp->tiles.count();
   const long long sets = (long long)p->B * p->G * dp->nrc;
+  // Chunks of at most 32 rows: every wave of a 4-wave workgroup is a partial over its own
+  // tiles (one workgroup per CU, 128 KiB of LDS), at least 2 tiles per wave.  Larger chunks:
+  // one wave per 32-row block sharing the tiles, the workgroup a partial (64 KiB of LDS, two
+  // per CU), at least 4 tiles per workgroup.
+  dp->shared_tiles = rows > 32 ? 1 : 0;
   const int cus = current_cu_count();
-  long long nsplit = cus > 0 ? (cus + sets - 1) / sets : 1;
-  const long long cap = nt / 8 > 1 ? nt / 8 : 1;
+  const long long target = cus > 0 ? (long long)cus * (dp->shared_tiles ? 2 : 1) : 1;
+  long long nsplit = (target + sets - 1) / sets;
+  const long long min_tiles = dp->shared_tiles ? 4 : 8;
+  const long long cap = nt / min_tiles > 1 ? nt / min_tiles : 1;
   if (nsplit > cap) nsplit = cap;
   if (nsplit < 1) nsplit = 1;
   dp->nsplit = (int)nsplit;
+  dp->n_part = (int)(nsplit * (dp->shared_tiles ? 1 : kDecodeWaves));
   if (!grid_ok(sets * nsplit) || !grid_ok(((long long)p->B * p->H * p->Sq + 3) / 4)) return GQA_ERR_UNSUPPORTED;
-  const size_t parts = (size_t)sets * nsplit * kDecodeWaves;
+  const size_t parts = (size_t)sets * dp->n_part;
   const size_t bytes = parts * ((size_t)kDecodeRows * gqa::kHeadDim + 2 * kDecodeRows) * sizeof(float);
   *ws_bytes = (bytes + 255) & ~(size_t)255;
   return GQA_OK;
@@ -365,7 +372,7 @@ int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, c
   dp.v = v;
   dp.o = o;
   dp.lse = lse;
-  const size_t parts = (size_t)p->B * p->G * dp.nrc * dp.nsplit * gqa::kDecodeWaves;
+  const size_t parts = (size_t)p->B * p->G * dp.nrc * dp.n_part;
   dp.part_o = (float*)workspace;
   dp.part_ml = dp.part_o + parts * gqa::kDecodeRows * gqa::kHeadDim;
   return hip_status(gqa::launch_decode(dp, p->dtype, (hipStream_t)stream));

@@ -177,7 +177,10 @@ struct DecodeParams {
   int hpg;           // H / G
   int rows;          // hpg * Sq
   int nrc;           // row chunks per (b, g) = ceil(rows / kDecodeRows)
-  int nsplit;        // workgroups per (b, g, chunk); partials per set = 4 * nsplit
+  int nsplit;        // workgroups per (b, g, chunk)
+  int shared_tiles;  // 0: each of a workgroup's 4 waves is a partial (chunks of <= 32 rows);
+                     // 1: one wave per 32-row block sharing the tiles, the workgroup a partial
+  int n_part;        // partials per set: 4 * nsplit, or nsplit when shared_tiles
   float scale_log2;  // scale * log2(e)
   MaskSpec mask;     // S = Skv, causal
   TileRanges tiles;  // key tiles visible to at least one row (sinks, then window)
