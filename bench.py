@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PFLOP/s dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal GQA attention TFLOP/s (fwd, bwd) at d=64 + % of MI355X bf16 MFMA peak"
-KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_device.h", "gqa_internal.h"]
+KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_device.h",
+                  "gqa_internal.h"]
 
 
 def parse_args():
@@ -47,6 +48,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="step",
                     choices=["step", "c2", "c3", "c4", "c5", "long", "decode", "decode16"])
+    ap.add_argument("--rope", action="store_true",
+                    help="YaRN RoPE (factor 32) on q and k in front of attention: rotation of K, the "
+                         "forward with Q rotated in registers, and dQ / dK rotated back after the backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -92,7 +96,7 @@ def load_traffic(kernel, wname):
     return ent.get("bytes_per_launch")
 
 
-KERNEL_KEYS = {"fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
+KERNEL_KEYS = {"rope_kernel": "rope", "fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
                "bwd_fused_kernel": "bwd_grads", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq",
                "decode_split_kernel": "decode", "decode_merge_kernel": "decode_merge", "copyBuffer": "copy"}
 COPY_BYTES = 1 << 30
@@ -140,7 +144,7 @@ def reduce_counters(fetch_csv, write_csv, wname):
     print(json.dumps(rec["kernels"], indent=1))
 
 
-def cpu_baseline(w, inputs, budget_s):
+def cpu_baseline(w, inputs, budget_s, rope=False):
     """The oracle, as it stands, on whole kv groups of the same workload until the
     time budget is used: forward rows of every head of the group plus its backward.
     At the long-context workload one group alone would take hours, so there it times
@@ -150,6 +154,9 @@ def cpu_baseline(w, inputs, budget_s):
 
     import oracle.attention as ref
     from transformer_attention_07_amd import gqa_visible_pairs
+
+    if rope:
+        import oracle.rope as ref  # the same entry points, with the rotation in front
 
     q, k, v, do = inputs
     if w.per_slab:
@@ -322,6 +329,8 @@ def main():
         sys.exit(1)
     gqa.library()  # fail loudly if the HIP library is not built
     w = workload(args.workload)
+    if args.rope:
+        w = w.with_(name=w.name + "_rope")
     do_bwd = "bwd" in w.direction
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
     q, k, v, do = make_inputs(w, with_do=do_bwd)
@@ -339,15 +348,31 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     kernels = ["fwd"] + (["bwd_preprocess", "bwd_grads"] if do_bwd else [])
+    q_rot = k_rot = None
+    if args.rope:
+        # the rotated Q (kept for the backward) and K; the backward rotates dQ and dK back as
+        # its kernels store them
+        q_rot = torch.empty_like(qd) if do_bwd else None
+        k_rot = torch.empty_like(kd)
+        ws = torch.empty(max(gqa.gqa_attn_bwd_workspace_bytes(qd, kd, **kw), 16), dtype=torch.uint8, device=dev)
+        kernels = ["fwd_rope"] + (["bwd_rope"] if do_bwd else [])
 
     def step(events=None):
         def mark(i):
             if events is not None:
                 events[i].record(stream)
         mark(0)
-        gqa.gqa_attn_fwd(qd, kd, vd, out=o, lse=lse, o_lo=o_lo, stream=stream, **kw)
+        if args.rope:  # rotation of K, then the forward with Q rotated in registers
+            gqa.gqa_attn_fwd_rope(qd, kd, vd, out=o, lse=lse, o_lo=o_lo, q_rot=q_rot, k_rot=k_rot,
+                                  keep_q_rot=do_bwd, stream=stream, **kw)
+        else:
+            gqa.gqa_attn_fwd(qd, kd, vd, out=o, lse=lse, o_lo=o_lo, stream=stream, **kw)
         mark(1)
-        if do_bwd:
+        if do_bwd and args.rope:  # delta, then dK/dV and dQ with the back-rotation at the store
+            gqa.gqa_attn_bwd_rope(q_rot, k_rot, vd, o, lse, dod, dq=dq, dk=dk, dv=dv, workspace=ws, o_lo=o_lo,
+                                  stream=stream, **kw)
+            mark(2)
+        elif do_bwd:
             gqa.gqa_attn_bwd_preprocess(o, dod, delta=delta, o_lo=o_lo, stream=stream)
             mark(2)
             # dK, dV and dQ: one fused launch when the dK/dV grid fits in one round of
@@ -380,7 +405,9 @@ def main():
 
     pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
     bh = w.B * w.H
-    flop = {"fwd": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0, "bwd_grads": 10.0 * w.D * pairs * bh}
+    # with --rope, fwd_rope is the rotation of K plus the forward, bwd_rope delta plus dK/dV and dQ
+    flop = {"fwd": 4.0 * w.D * pairs * bh, "fwd_rope": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0,
+            "bwd_grads": 10.0 * w.D * pairs * bh, "bwd_rope": 10.0 * w.D * pairs * bh}
     elem = 2 if w.dtype in ("bf16", "f16") else 4
     hbm_bytes = {"bwd_preprocess": 3.0 * bh * w.S * w.D * elem + bh * w.S * 4}  # O, o_lo, dO in; delta out
     step_flop = flop["fwd"] + (10.0 * w.D * pairs * bh if do_bwd else 0.0)
@@ -396,13 +423,15 @@ def main():
         else:
             d.update(gbs=round(hbm_bytes[name] / (ms * 1e-3) / 1e9, 1))
         detail[name] = d
-    fwd_tflops = flop["fwd"] / (per_kernel_ms["fwd"] * 1e-3) / 1e12
+    fwd_tflops = flop[kernels[0]] / (per_kernel_ms[kernels[0]] * 1e-3) / 1e12
     if do_bwd:
         bwd_ms = sum(per_kernel_ms[n] for n in kernels[1:])
         detail["bwd_total"] = {"ms": round(bwd_ms, 5),
                                "tflops": round(10.0 * w.D * pairs * bh / (bwd_ms * 1e-3) / 1e12, 1)}
     detail["fwd_tflops"] = round(fwd_tflops, 1)
 
+    # (with --rope the timed units are the two calls, each two launches; per-kernel times of
+    # that run come from the kernel trace)
     dominant = max((n for n in kernels if flop[n] > 0), key=lambda n: per_kernel_ms[n])
     ach = flop[dominant] / (per_kernel_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2),
@@ -413,10 +442,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, (q, k, v, do), args.cpu_seconds)
+        cpu = cpu_baseline(w, (q, k, v, do), args.cpu_seconds, rope=args.rope)
 
     wl = (f"causal GQA {'fwd+bwd' if do_bwd else 'fwd'}, B={w.B} H={w.H} G={w.G} S={w.S} d={w.D}"
-          + (f" window={w.window} sinks={w.num_sinks}" if w.window else "") + f", {w.dtype}")
+          + (f" window={w.window} sinks={w.num_sinks}" if w.window else "")
+          + (", YaRN RoPE x32 on q and k" if args.rope else "") + f", {w.dtype}")
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -424,7 +454,8 @@ def main():
         "data": "synthetic N(0,1), seeded",
         "config": {"workload": wl, "B": w.B, "H": w.H, "G": w.G, "S": w.S, "D": w.D, "causal": w.causal,
                    "window": w.window, "num_sinks": w.num_sinks, "visible_pairs_per_head": pairs,
-                   "flop_per_step": step_flop, "parallelism": "none (1 GPU)"},
+                   "flop_per_step": step_flop, "parallelism": "none (1 GPU)",
+                   "rope": dict(gqa.YARN_ROPE) if args.rope else None},
         "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernels": detail,
         "roofline": roofline,

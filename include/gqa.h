@@ -191,6 +191,63 @@ size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p);
 int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, const void* v,
                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Rotary position embedding with YaRN frequencies ("SnapKitty Transformer 8B" model card:
+ * YaRN RoPE, 32x factor, in the Model Specifications table; rope_yarn and
+ * rope_yarn_factor 32.0 with max_seq_len 204800 in its Training Configuration; YaRN-scaled
+ * RoPE inside the attention kernels in its Protected Inventions list).  The card gives no
+ * formula; this library follows the published methods it names:
+ *
+ *   RoFormer rotary embedding: the dimension pair (2i, 2i+1), i < D/2, of the vector at
+ *   position p is rotated by the angle p * theta'_i:
+ *       y_{2i}   = m (x_{2i} cos - x_{2i+1} sin),   y_{2i+1} = m (x_{2i} sin + x_{2i+1} cos)
+ *   YaRN frequencies ("NTK-by-parts"): theta_i = base^(-2i/D), r_i = orig_ctx theta_i / (2 pi),
+ *       gamma_i = clamp((r_i - alpha) / (beta - alpha), 0, 1),
+ *       theta'_i = (1 - gamma_i) theta_i / factor + gamma_i theta_i      (factor > 1)
+ *       theta'_i = theta_i                                               (factor == 1)
+ *   and m = YaRN's attention temperature 0.1 ln(factor) + 1 on each of q and k (or mscale).
+ *
+ * The model card's setting: base 10000, factor 32, orig_ctx 204800 / 32 = 6400, alpha 1,
+ * beta 32, mscale 0 (the YaRN value, 1.3466).  Base, the original context and the ramp
+ * bounds are the YaRN and RoFormer papers' values, not the card's.  The D/2 frequencies
+ * are worked out on the host in fp64 from this struct; each position's angles and the
+ * rotation run in the kernels, the angle reduced to one revolution in fp64 so that any
+ * position below 2^31 keeps fp32 accuracy. */
+typedef struct gqa_rope {
+  double base;     /* frequency base, > 1 (10000)                                        */
+  double factor;   /* YaRN context scale, >= 1; 1 = plain rotary embedding (32)          */
+  double orig_ctx; /* original context length of the ramp, > 0 when factor > 1 (6400)   */
+  double alpha;    /* pairs turning fewer than alpha times over orig_ctx: theta / factor  */
+  double beta;     /* pairs turning more than beta times keep theta; beta > alpha (1, 32) */
+  double mscale;   /* factor m on each rotated vector, >= 0; 0 = YaRN's 0.1 ln(factor) + 1 */
+} gqa_rope;
+
+/* y = m R(pos0 + s) x for every row s of x, or m R(pos0 + s)^T x with inverse = 1 (the
+ * backward of the rotation).  x, y: [n_slabs][S][D] rows of dtype (GQA_BF16, GQA_F16 or
+ * GQA_F32), device memory, 16-byte aligned, either the same buffer (in place) or not
+ * overlapping.  D == 64.  0 <= pos0 and pos0 + S <= 2^31 - 1.  Errors: GQA_ERR_INVALID_ARG
+ * for a bad configuration, size, pointer or flag; GQA_ERR_UNSUPPORTED for D != 64;
+ * GQA_ERR_HIP if the launch fails.  n_slabs == 0 or S == 0 returns GQA_OK, no launch. */
+int gqa_rope_apply(const gqa_rope* r, const void* x, void* y, int64_t n_slabs, int32_t S, int32_t D,
+                   int64_t pos0, int32_t inverse, int32_t dtype, void* stream);
+
+/* Forward with the rotation in front: O = attention(R Q, R K, V), query and key i at
+ * position i.  K is rotated into k_rot ([B][G][S][D], dtype; required), which is what the
+ * backward reads and what a key/value cache holds.  Q is rotated in the forward kernel's
+ * registers (never stored) unless q_rot is given ([B][H][S][D], dtype; NULL to skip), which
+ * then receives the rotated Q for the backward.  Everything else as gqa_attn_fwd; q_rot and
+ * k_rot must not overlap the inputs.  The rotated operands are rounded to dtype. */
+int gqa_attn_fwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q, const void* k, const void* v,
+                      void* o, void* o_lo, float* lse, void* q_rot, void* k_rot, void* stream);
+
+/* Backward of gqa_attn_fwd_rope: dQ, dK, dV of L = <O, dO> with respect to the unrotated
+ * Q, K and V.  Takes the rotated q_rot and k_rot of the forward; runs gqa_attn_bwd on them
+ * (which yields the gradients with respect to R Q and R K), then rotates dQ and dK back in
+ * place with m R^T.  Workspace and errors as gqa_attn_bwd (gqa_attn_bwd_workspace_bytes). */
+int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot, const void* k_rot,
+                      const void* v, const void* o, const void* o_lo, const float* lse, const void* d_o,
+                      float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

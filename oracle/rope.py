@@ -29,6 +29,12 @@ these readings (each is a choice where the card is silent):
   same sequence); in decode, query row t sits at Skv - Sq + t.
 * The backward of y = m R(p) x is dx = m R(p)^T dy, so dQ and dK are the attention
   gradients with respect to the rotated Q and K, rotated back.
+* ``operand_dtype``: the library's interface stores the rotated q and k in the input
+  element type (its rotated-key output is what a key/value cache holds), so for 16-bit
+  inputs the attention runs over those roundings.  With ``operand_dtype`` set (a torch
+  dtype) the oracle rounds its fp64 rotation the same way -- to fp32, then to that type,
+  each to nearest even, by PyTorch's conversions -- before the attention; with None it
+  uses the exact rotation.
 """
 
 from __future__ import annotations
@@ -95,85 +101,116 @@ def rope(x, positions, inverse: bool = False, cfg: YarnConfig = YARN) -> np.ndar
     return yarn_mscale(cfg) * _rotate_pairs(x, -ang if inverse else ang)
 
 
-def _rot_qk(q, k, cfg):
+def _stored(x, operand_dtype):
+    """x as the library stores a rotated operand: unchanged for None, else rounded to fp32
+    and then to ``operand_dtype`` (nearest even, PyTorch's conversions), back in fp64."""
+    if operand_dtype is None:
+        return x
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(operand_dtype)
+    return t.to(torch.float64).numpy()
+
+
+def _rot(x, positions, cfg, operand_dtype):
+    return _stored(rope(x, positions, cfg=cfg), operand_dtype)
+
+
+def _rot_qk(q, k, cfg, operand_dtype=None):
     S = q.shape[2]
     pos = np.arange(S)
-    return rope(q, pos, cfg=cfg), rope(k, pos, cfg=cfg)
+    return _rot(q, pos, cfg, operand_dtype), _rot(k, pos, cfg, operand_dtype)
 
 
-def forward(q, k, v, scale=None, causal=True, window=0, num_sinks=0, cfg: YarnConfig = YARN):
+def forward(q, k, v, scale=None, causal=True, window=0, num_sinks=0, cfg: YarnConfig = YARN,
+            operand_dtype=None):
     """O [B,H,S,D] and lse [B,H,S] of attention over the rotated q and k, fp64."""
-    qr, kr = _rot_qk(q, k, cfg)
+    qr, kr = _rot_qk(q, k, cfg, operand_dtype)
     return attn.forward(qr, kr, v, scale, causal, window, num_sinks)
 
 
 def forward_rows(q, k, v, b: int, h: int, rows, scale=None, causal=True, window=0, num_sinks=0,
-                 cfg: YarnConfig = YARN):
+                 cfg: YarnConfig = YARN, operand_dtype=None):
     """O[b, h, rows, :] and lse[b, h, rows] with the rotation: the rows of q are rotated
     at their positions and the whole key slab of their kv head at 0 .. S-1."""
     B, H, S, D = q.shape
     g = int(attn.kv_head(h, H, k.shape[1]))
     rows = np.asarray(rows, dtype=np.int64)
     qr = np.zeros((1, 1, S, D))
-    qr[0, 0, rows] = rope(attn._f64(q[b, h, rows]), rows, cfg=cfg)
-    kr = rope(attn._f64(k[b, g]), np.arange(S), cfg=cfg)[None, None]
+    qr[0, 0, rows] = _rot(attn._f64(q[b, h, rows]), rows, cfg, operand_dtype)
+    kr = _rot(attn._f64(k[b, g]), np.arange(S), cfg, operand_dtype)[None, None]
     return attn.forward_rows(qr, kr, attn._f64(v[b, g])[None, None], 0, 0, rows, scale, causal, window,
                              num_sinks)
 
 
-def backward(q, k, v, do, scale=None, causal=True, window=0, num_sinks=0, cfg: YarnConfig = YARN):
+def backward(q, k, v, do, scale=None, causal=True, window=0, num_sinks=0, cfg: YarnConfig = YARN,
+             operand_dtype=None):
     """dQ, dK, dV of L = <O, dO> through the rotation, fp64: the attention gradients with
     respect to the rotated q and k, rotated back with m R^T."""
     S = q.shape[2]
-    qr, kr = _rot_qk(q, k, cfg)
+    qr, kr = _rot_qk(q, k, cfg, operand_dtype)
     dqr, dkr, dv = attn.backward(qr, kr, v, do, scale, causal, window, num_sinks)
     pos = np.arange(S)
     return rope(dqr, pos, inverse=True, cfg=cfg), rope(dkr, pos, inverse=True, cfg=cfg), dv
 
 
-def _group_rotated(q, k, b, g, cfg):
+def _group_rotated(q, k, b, g, cfg, operand_dtype=None):
     """Rotated q slabs of the heads of kv group g and the rotated k slab, as [1,hpg,S,D]
     and [1,1,S,D] arrays (kv head 0 of a one-group problem)."""
     B, H, S, D = q.shape
     hpg = H // k.shape[1]
     pos = np.arange(S)
-    qr = rope(attn._f64(q[b, g * hpg:(g + 1) * hpg]), pos, cfg=cfg)[None]
-    kr = rope(attn._f64(k[b, g]), pos, cfg=cfg)[None, None]
+    qr = _rot(attn._f64(q[b, g * hpg:(g + 1) * hpg]), pos, cfg, operand_dtype)[None]
+    kr = _rot(attn._f64(k[b, g]), pos, cfg, operand_dtype)[None, None]
     return qr, kr
 
 
+def backward_group(q, k, v, do, b: int, g: int, scale=None, causal=True, window=0, num_sinks=0,
+                   cfg: YarnConfig = YARN, operand_dtype=None):
+    """dQ [H/G, S, D] of the heads of kv group g (in head order) and dK, dV [S, D] of that
+    kv head, through the rotation, fp64."""
+    B, H, S, D = q.shape
+    hpg = H // k.shape[1]
+    qr, kr = _group_rotated(q, k, b, g, cfg, operand_dtype)
+    dqr, dkr, dv = attn.backward_group(qr, kr, attn._f64(v[b, g])[None, None],
+                                       attn._f64(do[b, g * hpg:(g + 1) * hpg])[None], 0, 0, scale, causal,
+                                       window, num_sinks)
+    pos = np.arange(S)
+    return rope(dqr, pos, inverse=True, cfg=cfg), rope(dkr, pos, inverse=True, cfg=cfg), dv
+
+
 def backward_rows(q, k, v, do, b: int, h: int, rows, scale=None, causal=True, window=0, num_sinks=0,
-                  cfg: YarnConfig = YARN):
+                  cfg: YarnConfig = YARN, operand_dtype=None):
     """dQ[b, h, rows, :] through the rotation, fp64."""
     B, H, S, D = q.shape
     G = k.shape[1]
     g = int(attn.kv_head(h, H, G))
     rows = np.asarray(rows, dtype=np.int64)
-    qr = rope(attn._f64(q[b, h]), np.arange(S), cfg=cfg)[None, None]
-    kr = rope(attn._f64(k[b, g]), np.arange(S), cfg=cfg)[None, None]
+    qr = _rot(attn._f64(q[b, h]), np.arange(S), cfg, operand_dtype)[None, None]
+    kr = _rot(attn._f64(k[b, g]), np.arange(S), cfg, operand_dtype)[None, None]
     dqr = attn.backward_rows(qr, kr, attn._f64(v[b, g])[None, None], attn._f64(do[b, h])[None, None], 0, 0,
                              rows, scale, causal, window, num_sinks)
     return rope(dqr, rows, inverse=True, cfg=cfg)
 
 
 def backward_keys(q, k, v, do, b: int, g: int, keys, scale=None, causal=True, window=0, num_sinks=0,
-                  cfg: YarnConfig = YARN):
+                  cfg: YarnConfig = YARN, operand_dtype=None):
     """dK[b, g, keys, :] and dV[b, g, keys, :] through the rotation, fp64."""
     B, H, S, D = q.shape
     hpg = H // k.shape[1]
     keys = np.asarray(keys, dtype=np.int64)
-    qr, kr = _group_rotated(q, k, b, g, cfg)
+    qr, kr = _group_rotated(q, k, b, g, cfg, operand_dtype)
     dkr, dv = attn.backward_keys(qr, kr, attn._f64(v[b, g])[None, None],
                                  attn._f64(do[b, g * hpg:(g + 1) * hpg])[None], 0, 0, keys, scale, causal,
                                  window, num_sinks)
     return rope(dkr, keys, inverse=True, cfg=cfg), dv
 
 
-def decode(q, k, v, scale=None, window=0, num_sinks=0, cfg: YarnConfig = YARN):
+def decode(q, k, v, scale=None, window=0, num_sinks=0, cfg: YarnConfig = YARN, operand_dtype=None):
     """Decode through the rotation: query row t at position Skv - Sq + t, cache key j at
     position j (the cache holds unrotated keys here; rotating them is part of the
     computation checked)."""
     Sq, Skv = q.shape[2], k.shape[2]
-    qr = rope(q, np.arange(Skv - Sq, Skv), cfg=cfg)
-    kr = rope(k, np.arange(Skv), cfg=cfg)
+    qr = _rot(q, np.arange(Skv - Sq, Skv), cfg, operand_dtype)
+    kr = _rot(k, np.arange(Skv), cfg, operand_dtype)
     return attn.decode(qr, kr, v, scale, window, num_sinks)

@@ -1,7 +1,7 @@
 """Pins for the rotary-embedding oracle (``oracle.rope``): each check takes an
 implementation module exposing ``rope``, ``rope_frequencies``, ``yarn_frequencies``,
-``yarn_mscale``, ``forward``, ``forward_rows``, ``backward``, ``backward_rows``,
-``backward_keys``, ``decode`` and the configurations ``YARN`` / ``PLAIN``, and raises
+``yarn_mscale``, ``forward``, ``forward_rows``, ``backward``, ``backward_group``,
+``backward_rows``, ``backward_keys``, ``decode`` and the configurations ``YARN`` / ``PLAIN``, and raises
 AssertionError when it disagrees with what the published methods or the mathematics fix.
 tests/test_oracle_mutants.py plants mistakes in copies of the oracle to show the checks
 catch them.
@@ -224,6 +224,10 @@ def check_rows_keys_and_decode(impl):
             dkr, dvr = impl.backward_keys(q, k, v, do, b, g, keys, **kw)
             assert np.allclose(dkr, dk[b, g, keys], rtol=0, atol=1e-11)
             assert np.allclose(dvr, dv[b, g, keys], rtol=0, atol=1e-11)
+            dqg, dkg, dvg = impl.backward_group(q, k, v, do, b, g, **kw)
+            hpg = H // G
+            assert np.allclose(dqg, dq[b, g * hpg:(g + 1) * hpg], rtol=0, atol=1e-11)
+            assert np.allclose(dkg, dk[b, g], rtol=0, atol=1e-11) and np.allclose(dvg, dv[b, g], rtol=0, atol=1e-11)
     # decode of the newest Sq rows is the forward's last Sq rows
     for Sq in (1, 4, S):
         Od, ld = impl.decode(q[:, :, S - Sq:], k, v, window=W, num_sinks=NS)
@@ -231,6 +235,41 @@ def check_rows_keys_and_decode(impl):
         assert np.allclose(ld, lse[:, :, S - Sq:], rtol=0, atol=1e-12), Sq
 
 
+def _bf16_nearest_even(x):
+    """fp64 -> fp32 -> bf16, each to nearest even, by integer arithmetic on the fp32 bits
+    (finite values), back in fp64."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def check_stored_operands(impl):
+    # with operand_dtype = bf16 the attention runs over the bf16 roundings of the rotated
+    # q and k (and nothing else is rounded): against PyTorch's attention over operands
+    # rounded by the integer rule above
+    rng = _rng(47)
+    B, H, G, S, D, W, NS = 1, 4, 2, 40, 64, 9, 3
+    qn, kn, vn, don = (_rand(rng, B, H, S, D), _rand(rng, B, G, S, D), _rand(rng, B, G, S, D),
+                       _rand(rng, B, H, S, D))
+    pos = np.arange(S)
+    qr = torch.tensor(_bf16_nearest_even(impl.rope(qn, pos)), requires_grad=True)
+    kr = torch.tensor(_bf16_nearest_even(impl.rope(kn, pos)), requires_grad=True)
+    v = torch.tensor(vn)
+    mask = _range_mask(S, True, W, NS)
+    o = F.scaled_dot_product_attention(qr, kr, v, attn_mask=mask, scale=1.0 / 8.0, enable_gqa=True)
+    (o * torch.tensor(don)).sum().backward()
+    kw = dict(window=W, num_sinks=NS, operand_dtype=torch.bfloat16)
+    O, _ = impl.forward(qn, kn, vn, **kw)
+    dq, dk, _ = impl.backward(qn, kn, vn, don, **kw)
+    assert np.allclose(O, o.detach().numpy(), rtol=0, atol=1e-11)
+    # the gradients with respect to the rounded rotated operands, rotated back
+    assert np.allclose(dq, impl.rope(qr.grad.numpy(), pos, inverse=True), rtol=0, atol=1e-10)
+    assert np.allclose(dk, impl.rope(kr.grad.numpy(), pos, inverse=True), rtol=0, atol=1e-10)
+    # and the rounding matters: the exact rotation gives a different O
+    O_exact, _ = impl.forward(qn, kn, vn, window=W, num_sinks=NS)
+    assert np.abs(O_exact - O).max() > 1e-4
+
+
 ALL_ROPE_CHECKS = [check_plain_frequencies, check_complex_form, check_mscale_and_identities,
                    check_relative_position, check_yarn_regions, check_attention_vs_torch,
-                   check_rope_fd_gradients, check_rows_keys_and_decode]
+                   check_rope_fd_gradients, check_rows_keys_and_decode, check_stored_operands]

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 15, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -174,3 +174,83 @@ def test_visible_pairs_at_workload_sizes():
     S, W, NS = 65536, 16384, 2048
     by_rows = sum(min(i + 1, W) + min(NS, max(0, i - W + 1)) for i in range(S))
     assert gqa.gqa_visible_pairs(S, True, W, NS) == by_rows == 1038099456
+
+
+# ---- rotary embedding entry points: validation only (no launch) ----
+def _rope_apply(r, x=FAKE, y=FAKE, n=4, S=128, D=64, pos0=0, inverse=0, dtype=binding.GQA_BF16):
+    return gqa.library().gqa_rope_apply(None if r is None else ctypes.byref(r), x, y, n, S, D, pos0, inverse, dtype,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(base=1.0), binding.GQA_ERR_INVALID_ARG),
+    (dict(base=float("nan")), binding.GQA_ERR_INVALID_ARG),
+    (dict(factor=0.5), binding.GQA_ERR_INVALID_ARG),
+    (dict(factor=float("inf")), binding.GQA_ERR_INVALID_ARG),
+    (dict(mscale=-1.0), binding.GQA_ERR_INVALID_ARG),
+    (dict(orig_ctx=0.0), binding.GQA_ERR_INVALID_ARG),
+    (dict(alpha=32.0, beta=32.0), binding.GQA_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), binding.GQA_ERR_INVALID_ARG),
+])
+def test_rope_config_validation(kw, status):
+    r = gqa.make_rope(**kw)
+    assert _rope_apply(r, x=None) == status      # the configuration is checked first
+    p = gqa.make_problem(1, 4, 2, 128)
+    lib = gqa.library()
+    assert lib.gqa_attn_fwd_rope(ctypes.byref(p), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                                 None) == status
+    assert lib.gqa_attn_bwd_rope(ctypes.byref(p), ctypes.byref(r), *([FAKE] * 5), None, *([FAKE] * 5), FAKE,
+                                 1 << 40, None) == status
+
+
+def test_rope_plain_factor_ignores_ramp_fields():
+    # with factor 1 the ramp is unused, so its fields are not checked (empty call: no launch)
+    r = gqa.make_rope(factor=1.0, orig_ctx=0.0, alpha=5.0, beta=1.0)
+    assert _rope_apply(r, n=0) == binding.GQA_OK
+
+
+def test_rope_apply_argument_checks():
+    r = gqa.make_rope()
+    I = binding.GQA_ERR_INVALID_ARG
+    assert _rope_apply(None) == I
+    assert _rope_apply(r, dtype=7) == I
+    assert _rope_apply(r, n=-1) == I
+    assert _rope_apply(r, S=-1) == I
+    assert _rope_apply(r, pos0=-1) == I
+    assert _rope_apply(r, pos0=2 ** 31 - 100, S=128) == I     # positions past 2^31 - 1
+    assert _rope_apply(r, inverse=2) == I
+    assert _rope_apply(r, D=128) == binding.GQA_ERR_UNSUPPORTED
+    assert _rope_apply(r, x=None) == I
+    assert _rope_apply(r, y=FAKE + 8) == I                      # misaligned
+    assert _rope_apply(r, y=FAKE + 128) == I                    # partial overlap with x
+    for n, S in [(0, 128), (4, 0)]:
+        assert _rope_apply(r, x=None, y=None, n=n, S=S) == binding.GQA_OK
+
+
+def test_fwd_bwd_rope_argument_checks():
+    lib = gqa.library()
+    r = gqa.make_rope()
+    p = gqa.make_problem(1, 4, 2, 128)
+    I = binding.GQA_ERR_INVALID_ARG
+    kbytes = 1 * 2 * 128 * 64 * 2
+    base = dict(q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), o=FAKE + (3 << 24), o_lo=None,
+                lse=FAKE + (4 << 24), q_rot=None, k_rot=FAKE + (5 << 24))
+
+    def fwd(**kw):
+        a = dict(base, **kw)
+        return lib.gqa_attn_fwd_rope(ctypes.byref(p), ctypes.byref(r), a["q"], a["k"], a["v"], a["o"], a["o_lo"],
+                                     a["lse"], a["q_rot"], a["k_rot"], None)
+    assert fwd(k_rot=None) == I
+    assert fwd(q_rot=FAKE + 8) == I                              # misaligned
+    assert fwd(k_rot=base["k"]) == I                             # k_rot is the input k
+    assert fwd(k_rot=base["k"] + kbytes - 16) == I               # k_rot overlaps k
+    assert fwd(q_rot=base["k_rot"]) == I                         # q_rot overlaps k_rot
+    assert lib.gqa_attn_fwd_rope(ctypes.byref(p), None, *([FAKE] * 4), None, FAKE, None, FAKE, None) == I
+    e = gqa.make_problem(0, 4, 2, 128)
+    assert lib.gqa_attn_fwd_rope(ctypes.byref(e), ctypes.byref(r), *([None] * 8), None) == binding.GQA_OK
+    # backward: the workspace is checked as for gqa_attn_bwd
+    need = lib.gqa_attn_bwd_workspace_bytes(ctypes.byref(p))
+    args = [ctypes.byref(p), ctypes.byref(r)] + [FAKE] * 4 + [None] + [FAKE] * 5
+    assert lib.gqa_attn_bwd_rope(*args, None, need, None) == binding.GQA_ERR_WORKSPACE
+    assert lib.gqa_attn_bwd_rope(*args, FAKE, need - 1, None) == binding.GQA_ERR_WORKSPACE
+    assert lib.gqa_attn_bwd_rope(ctypes.byref(e), ctypes.byref(r), *([None] * 10), None, 0, None) == binding.GQA_OK

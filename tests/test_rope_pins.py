@@ -96,15 +96,27 @@ def _mut_positions_from_one(x, positions, inverse=False, cfg=rr.YARN):
     return _orig_rope(x, pos + (1 if pos.size and pos.size < 40 and pos.min() > 0 else 0), inverse, cfg)
 
 
-def _mut_rot_v_too(q, k, cfg):
+def _mut_rot_v_too(q, k, cfg, operand_dtype=None):
     S = q.shape[2]
     pos = np.arange(S)
     return _orig_rope(q, pos, cfg=cfg), _orig_rope(k, pos, cfg=cfg)[..., ::-1].copy()
 
 
-def _mut_only_q(q, k, cfg):
+def _mut_only_q(q, k, cfg, operand_dtype=None):
     S = q.shape[2]
     return _orig_rope(q, np.arange(S), cfg=cfg), rr.attn._f64(k)
+
+
+def _mut_stored_truncated(x, operand_dtype):
+    # rounding toward zero instead of to nearest
+    if operand_dtype is None:
+        return x
+    b = x.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _mut_stored_ignored(x, operand_dtype):
+    return x
 
 
 MUTANTS = {
@@ -123,6 +135,8 @@ MUTANTS = {
     "row_positions_off_by_one": ("rope", _mut_positions_from_one),
     "keys_rotated_wrongly": ("_rot_qk", _mut_rot_v_too),
     "keys_not_rotated": ("_rot_qk", _mut_only_q),
+    "stored_operands_truncated": ("_stored", _mut_stored_truncated),
+    "stored_operands_not_rounded": ("_stored", _mut_stored_ignored),
 }
 
 

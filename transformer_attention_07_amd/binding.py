@@ -26,7 +26,8 @@ _DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_
 EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
             "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads",
-            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode")
+            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_rope_apply",
+            "gqa_attn_fwd_rope", "gqa_attn_bwd_rope")
 
 
 class GqaError(RuntimeError):
@@ -47,6 +48,28 @@ class gqa_decode_problem(ctypes.Structure):
                 ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class gqa_rope(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("factor", ctypes.c_double), ("orig_ctx", ctypes.c_double),
+                ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("mscale", ctypes.c_double)]
+
+
+# The model card's setting: YaRN factor 32 over a 204,800-token context (original context
+# 6,400); base and ramp bounds from the RoFormer and YaRN papers; mscale 0 = YaRN's value.
+YARN_ROPE = dict(base=10000.0, factor=32.0, orig_ctx=6400.0, alpha=1.0, beta=32.0, mscale=0.0)
+
+
+def make_rope(base=10000.0, factor=32.0, orig_ctx=6400.0, alpha=1.0, beta=32.0, mscale=0.0) -> gqa_rope:
+    return gqa_rope(float(base), float(factor), float(orig_ctx), float(alpha), float(beta), float(mscale))
+
+
+def _rope_arg(rope) -> gqa_rope:
+    if rope is None:
+        return make_rope()
+    if isinstance(rope, gqa_rope):
+        return rope
+    return make_rope(**rope)
 
 
 _lib = None
@@ -88,6 +111,14 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes.argtypes = [DP]
     lib.gqa_attn_decode.restype = ctypes.c_int
     lib.gqa_attn_decode.argtypes = [DP, vp, vp, vp, vp, fp, vp, ctypes.c_size_t, vp]
+    RP = ctypes.POINTER(gqa_rope)
+    lib.gqa_rope_apply.restype = ctypes.c_int
+    lib.gqa_rope_apply.argtypes = [RP, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_int32, ctypes.c_int32, vp]
+    lib.gqa_attn_fwd_rope.restype = ctypes.c_int
+    lib.gqa_attn_fwd_rope.argtypes = [P, RP, vp, vp, vp, vp, vp, fp, vp, vp, vp]
+    lib.gqa_attn_bwd_rope.restype = ctypes.c_int
+    lib.gqa_attn_bwd_rope.argtypes = [P, RP, vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -356,3 +387,104 @@ def gqa_attn_decode(q, k, v, window=0, num_sinks=0, scale=None, out=None, lse=No
     _check(library().gqa_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                      _ptr(workspace), ws_bytes, _stream(stream)), "gqa_attn_decode")
     return out, lse
+
+
+# ---- rotary position embedding (YaRN) ----
+def gqa_rope_apply(x, pos0=0, inverse=False, rope=None, out=None, stream=None):
+    """m R(pos0 + s) x (m R^T with ``inverse``) for x [..., S, 64] (bf16, f16 or fp32),
+    rows s along the second-to-last axis.  ``out`` may be x itself (in place)."""
+    if x.dim() < 2:
+        raise ValueError("x must be [..., S, D]")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _need(x, "x", device=x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", dtype=x.dtype, shape=x.shape, device=x.device)
+    S, D = x.shape[-2], x.shape[-1]
+    n = x.numel() // (S * D) if S * D else 0
+    r = _rope_arg(rope)
+    _check(library().gqa_rope_apply(ctypes.byref(r), _ptr(x), _ptr(out), n, S, D, int(pos0), int(bool(inverse)),
+                                    _DTYPES[x.dtype], _stream(stream)), "gqa_rope_apply")
+    return out
+
+
+def gqa_attn_fwd_rope(q, k, v, causal=True, window=0, num_sinks=0, scale=None, rope=None, out=None, lse=None,
+                      q_rot=None, k_rot=None, keep_q_rot=True, stream=None, o_lo=None, keep_residual=False):
+    """Attention over the rotated q and k (query and key i at position i).  Returns
+    (O, lse, q_rot, k_rot) and O's rounding residual last with ``keep_residual``; q_rot is
+    None unless ``keep_q_rot`` or a buffer is given."""
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype=q.dtype, device=q.device)
+    _need(v, "v", shape=k.shape)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    if q_rot is None and keep_q_rot:
+        q_rot = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, shape=q.shape, device=q.device)
+    _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
+    _need(k_rot, "k_rot", dtype=q.dtype, shape=k.shape, device=q.device)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dtype=q.dtype, shape=q.shape, device=q.device)
+    if keep_residual and o_lo is None:
+        o_lo = torch.empty_like(q)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
+    r = _rope_arg(rope)
+    _check(library().gqa_attn_fwd_rope(ctypes.byref(p), ctypes.byref(r), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                       _ptr(o_lo), _ptr(lse), _ptr(q_rot), _ptr(k_rot), _stream(stream)),
+           "gqa_attn_fwd_rope")
+    res = (out, lse, q_rot, k_rot)
+    return res + (o_lo,) if o_lo is not None else res
+
+
+def gqa_attn_bwd_rope(q_rot, k_rot, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale=None, rope=None,
+                      dq=None, dk=None, dv=None, workspace=None, stream=None, o_lo=None):
+    """dQ, dK, dV (fp32) with respect to the unrotated q, k, v, from the forward's rotated
+    q_rot and k_rot, O (and o_lo) and lse."""
+    p = _problem_from(q_rot, k_rot, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q_rot, k_rot, v, o, lse, d_o)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=q_rot.dtype, shape=q_rot.shape, device=q_rot.device)
+    dq, dk, dv = _grad_buffers(q_rot, k_rot, dq, dk, dv)
+    nbytes = int(library().gqa_attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q_rot.device)
+    _need(workspace, "workspace", device=q_rot.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    r = _rope_arg(rope)
+    _check(library().gqa_attn_bwd_rope(ctypes.byref(p), ctypes.byref(r), _ptr(q_rot), _ptr(k_rot), _ptr(v),
+                                       _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(workspace), ws_bytes, _stream(stream)), "gqa_attn_bwd_rope")
+    return dq, dk, dv
+
+
+class GqaAttentionRope(torch.autograd.Function):
+    """Autograd wrapper of attention with the YaRN rotation of q and k in front."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, window, num_sinks, scale, rope):
+        res = gqa_attn_fwd_rope(q, k, v, causal, window, num_sinks, scale, rope=rope,
+                                keep_residual=q.dtype != torch.float32)
+        o, lse, q_rot, k_rot = res[:4]
+        o_lo = res[4] if len(res) > 4 else None
+        ctx.save_for_backward(q_rot, k_rot, v, o, lse, o_lo)
+        ctx.cfg = (causal, window, num_sinks, scale, rope)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, d_o, d_lse):
+        q_rot, k_rot, v, o, lse, o_lo = ctx.saved_tensors
+        causal, window, num_sinks, scale, rope = ctx.cfg
+        dq, dk, dv = gqa_attn_bwd_rope(q_rot, k_rot, v, o, lse, d_o.contiguous().to(q_rot.dtype), causal,
+                                       window, num_sinks, scale, rope=rope, o_lo=o_lo)
+        return dq.to(q_rot.dtype), dk.to(k_rot.dtype), dv.to(v.dtype), None, None, None, None, None
+
+
+def gqa_attention_rope(q, k, v, causal=True, sliding_window=0, num_sinks=0, scale=None, rope=None):
+    """(O, lse) with autograd, q and k rotated by YaRN RoPE (``rope``: a dict of gqa_rope
+    fields or None for the model card's factor-32 setting)."""
+    return GqaAttentionRope.apply(q, k, v, causal, sliding_window, num_sinks, scale, rope)

@@ -92,6 +92,71 @@ int fill_bwd(const gqa_problem* p, BwdParams* bp) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
+// ---- rotary position embedding ----
+constexpr double kTwoPi = 6.28318530717958647693;
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (a == nullptr || b == nullptr) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bbytes && y < x + abytes;
+}
+
+size_t elem_bytes(int dtype) { return dtype == GQA_F32 ? 4 : 2; }
+
+// The configuration as the kernels take it: YaRN's per-pair frequencies (RoFormer's
+// base^(-2i/D), kept for pairs that turn more than beta times over the original context,
+// divided by the factor for those turning fewer than alpha times, linearly blended in
+// between), in revolutions per position, and the factor m on each rotated vector.
+int make_rope_spec(const gqa_rope* r, gqa::RopeSpec* spec) {
+  if (r == nullptr) return GQA_ERR_INVALID_ARG;
+  if (!(isfinite(r->base) && r->base > 1.0)) return GQA_ERR_INVALID_ARG;
+  if (!(isfinite(r->factor) && r->factor >= 1.0)) return GQA_ERR_INVALID_ARG;
+  if (!(isfinite(r->mscale) && r->mscale >= 0.0)) return GQA_ERR_INVALID_ARG;
+  if (r->factor > 1.0) {
+    if (!(isfinite(r->orig_ctx) && r->orig_ctx > 0.0)) return GQA_ERR_INVALID_ARG;
+    if (!(isfinite(r->alpha) && isfinite(r->beta) && r->beta > r->alpha)) return GQA_ERR_INVALID_ARG;
+  }
+  *spec = gqa::RopeSpec{};
+  const int D = gqa::kHeadDim;
+  for (int i = 0; i < D / 2; ++i) {
+    double theta = pow(r->base, -2.0 * i / D);
+    if (r->factor > 1.0) {
+      const double turns = r->orig_ctx * theta / kTwoPi;
+      double ramp = (turns - r->alpha) / (r->beta - r->alpha);
+      ramp = ramp < 0.0 ? 0.0 : ramp > 1.0 ? 1.0 : ramp;
+      theta = (1.0 - ramp) * theta / r->factor + ramp * theta;
+    }
+    spec->rev[i] = theta / kTwoPi;
+  }
+  const double m = r->mscale > 0.0 ? r->mscale : r->factor > 1.0 ? 0.1 * log(r->factor) + 1.0 : 1.0;
+  spec->mscale = (float)m;
+  spec->enabled = 1;
+  return GQA_OK;
+}
+
+// Launch plan of the rotation kernel: blocks of rows x runs of up to 16 slabs (the sines and
+// cosines of a run's rows are computed once), shorter runs while that leaves fewer than 8
+// blocks per compute unit.
+int plan_rope(const gqa::RopeSpec& spec, const void* x, void* y, long long n_slabs, int S, long long pos0,
+              int inverse, int dtype, gqa::RopeParams* rp) {
+  *rp = gqa::RopeParams{};
+  rp->x = x;
+  rp->y = y;
+  rp->n_slabs = n_slabs;
+  rp->S = S;
+  rp->pos0 = (int)pos0;
+  rp->inverse = inverse;
+  rp->spec = spec;
+  const int rows = gqa::rope_rows_per_block(dtype);
+  rp->n_row_blocks = (S + rows - 1) / rows;
+  const int cus = current_cu_count();
+  const long long want = 8LL * (cus > 0 ? cus : 256);
+  long long spb = 16;
+  while (spb > 1 && rp->n_row_blocks * ((n_slabs + spb - 1) / spb) < want) spb /= 2;
+  rp->slabs_per_block = (int)spb;
+  return grid_ok(rp->n_row_blocks * ((n_slabs + spb - 1) / spb)) ? GQA_OK : GQA_ERR_UNSUPPORTED;
+}
+
 
 // ---- decode ----
 int check_decode(const gqa_decode_problem* p) {
@@ -155,6 +220,121 @@ int plan_decode(const gqa_decode_problem* p, gqa::DecodeParams* dp, size_t* ws_b
   return GQA_OK;
 }
 
+
+// Forward launch with validated, non-empty arguments; rope == nullptr for plain attention.
+int run_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
+            const gqa::RopeSpec* rope, void* q_rot, hipStream_t s) {
+  FwdParams fp{};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.o = o;
+  fp.o_lo = o_lo;
+  fp.lse = lse;
+  fp.B = p->B;
+  fp.H = p->H;
+  fp.G = p->G;
+  fp.S = p->S;
+  fp.scale = p->scale;
+  fp.scale_log2 = p->scale * kLog2e;
+  fp.mask = normalised_mask(p);
+  row_decomposition(p, &fp.hpw, &fp.qpw, &fp.n_qblk);
+  if (rope != nullptr) {
+    fp.rope = *rope;
+    fp.q_rot = q_rot;
+  }
+  if (p->dtype == GQA_F32) return hip_status(gqa::launch_fwd_f32(fp, s));
+  return hip_status(gqa::launch_fwd_mfma(fp, p->dtype, s));
+}
+
+int fwd_grid_ok(const gqa_problem* p) {
+  if (p->dtype == GQA_F32) return grid_ok((long long)p->B * p->H * ((p->S + 63) / 64));
+  int hpw, qpw, n_qblk;
+  row_decomposition(p, &hpw, &qpw, &n_qblk);
+  return grid_ok((long long)n_qblk * p->B * (p->H / hpw));
+}
+
+
+int run_dkdv(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse, const void* d_o,
+             const float* delta, float* dk, float* dv, const gqa::RopeSpec* rope, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dk || !dv) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dk = dk;
+  bp.dv = dv;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dkdv_f32(bp, s));
+  return hip_status(gqa::launch_bwd_dkdv_mfma(bp, rope ? *rope : gqa::RopeSpec{}, p->dtype, s));
+}
+
+int run_dq(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse, const void* d_o,
+           const float* delta, float* dq, const gqa::RopeSpec* rope, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dq) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dq))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dq = dq;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dq_f32(bp, s));
+  return hip_status(gqa::launch_bwd_dq_mfma(bp, rope ? *rope : gqa::RopeSpec{}, p->dtype, s));
+}
+
+int run_grads(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse, const void* d_o,
+              const float* delta, float* dq, float* dk, float* dv, const gqa::RopeSpec* rope, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !lse || !d_o || !delta || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
+      !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return GQA_ERR_INVALID_ARG;
+  BwdParams bp;
+  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+  // When all dK/dV workgroups fit in one round of workgroup slots (two per CU), the causal
+  // spread of their work sets the pass's length; then dK/dV and dQ go in one launch and dQ
+  // workgroups fill the CUs that the short key blocks free.  Otherwise two launches.
+  const long long n_dkdv = (long long)bp.n_kblk * p->B * p->G;
+  const int cus = current_cu_count();
+  if (p->dtype == GQA_F32 || cus <= 0 || n_dkdv > 2LL * cus) {
+    if ((rc = run_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, rope, stream)) != GQA_OK) return rc;
+    return run_dq(p, q, k, v, lse, d_o, delta, dq, rope, stream);
+  }
+  if (!grid_ok(n_dkdv + (long long)bp.n_qblk * p->B * (p->H / bp.hpw))) return GQA_ERR_UNSUPPORTED;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.lse = lse;
+  bp.d_o = d_o;
+  bp.delta = delta;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  return hip_status(gqa::launch_bwd_fused_mfma(bp, rope ? *rope : gqa::RopeSpec{}, p->dtype, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +369,7 @@ int64_t gqa_visible_pairs(const gqa_problem* p) {
   return pairs;
 }
 
+
 int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, void* o_lo,
                  float* lse, void* stream) {
   int rc = check_problem(p);
@@ -198,29 +379,52 @@ int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_lo))
     return GQA_ERR_INVALID_ARG;
   if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
+  if (!fwd_grid_ok(p)) return GQA_ERR_UNSUPPORTED;
+  return run_fwd(p, q, k, v, o, o_lo, lse, nullptr, nullptr, (hipStream_t)stream);
+}
 
-  FwdParams fp{};
-  fp.q = q;
-  fp.k = k;
-  fp.v = v;
-  fp.o = o;
-  fp.o_lo = o_lo;
-  fp.lse = lse;
-  fp.B = p->B;
-  fp.H = p->H;
-  fp.G = p->G;
-  fp.S = p->S;
-  fp.scale = p->scale;
-  fp.scale_log2 = p->scale * kLog2e;
-  fp.mask = normalised_mask(p);
-  row_decomposition(p, &fp.hpw, &fp.qpw, &fp.n_qblk);
+int gqa_rope_apply(const gqa_rope* r, const void* x, void* y, int64_t n_slabs, int32_t S, int32_t D, int64_t pos0,
+                   int32_t inverse, int32_t dtype, void* stream) {
+  gqa::RopeSpec spec;
+  int rc = make_rope_spec(r, &spec);
+  if (rc != GQA_OK) return rc;
+  if (dtype != GQA_F32 && dtype != GQA_BF16 && dtype != GQA_F16) return GQA_ERR_INVALID_ARG;
+  if (n_slabs < 0 || S < 0 || D < 1 || pos0 < 0 || (inverse != 0 && inverse != 1)) return GQA_ERR_INVALID_ARG;
+  if (pos0 + (int64_t)S > (int64_t)INT_MAX) return GQA_ERR_INVALID_ARG;
+  if (D != gqa::kHeadDim) return GQA_ERR_UNSUPPORTED;
+  if (n_slabs == 0 || S == 0) return GQA_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return GQA_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)n_slabs * S * D * elem_bytes(dtype);
+  if (x != y && overlaps(x, bytes, y, bytes)) return GQA_ERR_INVALID_ARG;
+  gqa::RopeParams rp;
+  if ((rc = plan_rope(spec, x, y, n_slabs, S, pos0, inverse, dtype, &rp)) != GQA_OK) return rc;
+  return hip_status(gqa::launch_rope(rp, dtype, (hipStream_t)stream));
+}
+
+int gqa_attn_fwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q, const void* k, const void* v,
+                      void* o, void* o_lo, float* lse, void* q_rot, void* k_rot, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  gqa::RopeSpec spec;
+  if ((rc = make_rope_spec(r, &spec)) != GQA_OK) return rc;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q || !k || !v || !o || !lse || !k_rot) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_lo) ||
+      !aligned16(q_rot) || !aligned16(k_rot))
+    return GQA_ERR_INVALID_ARG;
+  if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
+  const size_t row = (size_t)p->D * elem_bytes(p->dtype);
+  const size_t qb = (size_t)p->B * p->H * p->S * row, kb = (size_t)p->B * p->G * p->S * row;
+  if (overlaps(k_rot, kb, q, qb) || overlaps(k_rot, kb, k, kb) || overlaps(k_rot, kb, v, kb) ||
+      overlaps(q_rot, qb, q, qb) || overlaps(q_rot, qb, k, kb) || overlaps(q_rot, qb, v, kb) ||
+      overlaps(q_rot, qb, k_rot, kb))
+    return GQA_ERR_INVALID_ARG;
+  if (!fwd_grid_ok(p)) return GQA_ERR_UNSUPPORTED;
+  gqa::RopeParams rp;
+  if ((rc = plan_rope(spec, k, k_rot, (long long)p->B * p->G, p->S, 0, 0, p->dtype, &rp)) != GQA_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (p->dtype == GQA_F32) {
-    if (!grid_ok((long long)p->B * p->H * ((p->S + 63) / 64))) return GQA_ERR_UNSUPPORTED;
-    return hip_status(gqa::launch_fwd_f32(fp, s));
-  }
-  if (!grid_ok((long long)fp.n_qblk * p->B * (p->H / fp.hpw))) return GQA_ERR_UNSUPPORTED;
-  return hip_status(gqa::launch_fwd_mfma(fp, p->dtype, s));
+  if ((rc = hip_status(gqa::launch_rope(rp, p->dtype, s))) != GQA_OK) return rc;
+  return run_fwd(p, q, k_rot, v, o, o_lo, lse, &spec, q_rot, s);
 }
 
 size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p) {
@@ -248,51 +452,20 @@ int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* o_l
   return hip_status(gqa::launch_bwd_preprocess(bp, p->dtype, (hipStream_t)stream));
 }
 
+
 int gqa_attn_bwd_dkdv(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
                       const void* d_o, const float* delta, float* dk, float* dv, void* stream) {
-  int rc = check_problem(p);
-  if (rc != GQA_OK) return rc;
-  if (empty_problem(p)) return GQA_OK;
-  if (!q || !k || !v || !lse || !d_o || !delta || !dk || !dv) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
-      !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
-    return GQA_ERR_INVALID_ARG;
-  BwdParams bp;
-  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
-  bp.q = q;
-  bp.k = k;
-  bp.v = v;
-  bp.lse = lse;
-  bp.d_o = d_o;
-  bp.delta = delta;
-  bp.dk = dk;
-  bp.dv = dv;
-  hipStream_t s = (hipStream_t)stream;
-  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dkdv_f32(bp, s));
-  return hip_status(gqa::launch_bwd_dkdv_mfma(bp, p->dtype, s));
+  return run_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, nullptr, stream);
 }
 
 int gqa_attn_bwd_dq(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
                     const void* d_o, const float* delta, float* dq, void* stream) {
-  int rc = check_problem(p);
-  if (rc != GQA_OK) return rc;
-  if (empty_problem(p)) return GQA_OK;
-  if (!q || !k || !v || !lse || !d_o || !delta || !dq) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
-      !aligned16(delta) || !aligned16(dq))
-    return GQA_ERR_INVALID_ARG;
-  BwdParams bp;
-  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
-  bp.q = q;
-  bp.k = k;
-  bp.v = v;
-  bp.lse = lse;
-  bp.d_o = d_o;
-  bp.delta = delta;
-  bp.dq = dq;
-  hipStream_t s = (hipStream_t)stream;
-  if (p->dtype == GQA_F32) return hip_status(gqa::launch_bwd_dq_f32(bp, s));
-  return hip_status(gqa::launch_bwd_dq_mfma(bp, p->dtype, s));
+  return run_dq(p, q, k, v, lse, d_o, delta, dq, nullptr, stream);
+}
+
+int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
+                       const void* d_o, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+  return run_grads(p, q, k, v, lse, d_o, delta, dq, dk, dv, nullptr, stream);
 }
 
 int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
@@ -311,40 +484,41 @@ int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void*
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   float* delta = (float*)workspace;
   if ((rc = gqa_attn_bwd_preprocess(p, o, o_lo, d_o, delta, stream)) != GQA_OK) return rc;
-  return gqa_attn_bwd_grads(p, q, k, v, lse, d_o, delta, dq, dk, dv, stream);
+  return run_grads(p, q, k, v, lse, d_o, delta, dq, dk, dv, nullptr, stream);
 }
 
-int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const void* v, const float* lse,
-                       const void* d_o, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot, const void* k_rot, const void* v,
+                      const void* o, const void* o_lo, const float* lse, const void* d_o, float* dq, float* dk,
+                      float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
   if (rc != GQA_OK) return rc;
+  gqa::RopeSpec spec;
+  if ((rc = make_rope_spec(r, &spec)) != GQA_OK) return rc;
   if (empty_problem(p)) return GQA_OK;
-  if (!q || !k || !v || !lse || !d_o || !delta || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
-      !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return GQA_ERR_INVALID_ARG;
-  BwdParams bp;
-  if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
-  // When all dK/dV workgroups fit in one round of workgroup slots (two per CU), the causal
-  // spread of their work sets the pass's length; then dK/dV and dQ go in one launch and dQ
-  // workgroups fill the CUs that the short key blocks free.  Otherwise two launches.
-  const long long n_dkdv = (long long)bp.n_kblk * p->B * p->G;
-  const int cus = current_cu_count();
-  if (p->dtype == GQA_F32 || cus <= 0 || n_dkdv > 2LL * cus) {
-    if ((rc = gqa_attn_bwd_dkdv(p, q, k, v, lse, d_o, delta, dk, dv, stream)) != GQA_OK) return rc;
-    return gqa_attn_bwd_dq(p, q, k, v, lse, d_o, delta, dq, stream);
+  if (p->dtype != GQA_F32) {
+    // 16-bit: the dK/dV and dQ kernels rotate their results back as they store them
+    if (!q_rot || !k_rot || !v || !o || !lse || !d_o || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q_rot) || !aligned16(k_rot) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+      return GQA_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+    BwdParams bp;
+    if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
+    float* delta = (float*)workspace;
+    if ((rc = gqa_attn_bwd_preprocess(p, o, o_lo, d_o, delta, stream)) != GQA_OK) return rc;
+    return run_grads(p, q_rot, k_rot, v, lse, d_o, delta, dq, dk, dv, &spec, stream);
   }
-  if (!grid_ok(n_dkdv + (long long)bp.n_qblk * p->B * (p->H / bp.hpw))) return GQA_ERR_UNSUPPORTED;
-  bp.q = q;
-  bp.k = k;
-  bp.v = v;
-  bp.lse = lse;
-  bp.d_o = d_o;
-  bp.delta = delta;
-  bp.dq = dq;
-  bp.dk = dk;
-  bp.dv = dv;
-  return hip_status(gqa::launch_bwd_fused_mfma(bp, p->dtype, (hipStream_t)stream));
+  // fp32: the backward, then the two back-rotations in place (plans checked before anything
+  // is enqueued)
+  gqa::RopeParams rq, rk;
+  if ((rc = plan_rope(spec, dq, dq, (long long)p->B * p->H, p->S, 0, 1, GQA_F32, &rq)) != GQA_OK) return rc;
+  if ((rc = plan_rope(spec, dk, dk, (long long)p->B * p->G, p->S, 0, 1, GQA_F32, &rk)) != GQA_OK) return rc;
+  rc = gqa_attn_bwd(p, q_rot, k_rot, v, o, o_lo, lse, d_o, dq, dk, dv, workspace, workspace_bytes, stream);
+  if (rc != GQA_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = hip_status(gqa::launch_rope(rq, GQA_F32, s))) != GQA_OK) return rc;
+  return hip_status(gqa::launch_rope(rk, GQA_F32, s));
 }
 
 size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p) {

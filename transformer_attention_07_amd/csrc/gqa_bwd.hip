@@ -236,6 +236,14 @@ __device__ __forceinline__ T* uni(T* ptr) {
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
   return (T*)((hi << 32) | lo);
 }
+// The kernels' second argument (the rotation table) in place in the kernel-argument
+// segment, so that the out-of-line passes read it there instead of taking a copy on each
+// lane's stack.  Only a kernel itself may call this: the segment pointer is not passed on
+// to called functions, which receive the table's address as an argument instead.
+__device__ __forceinline__ const RopeSpec* kernel_rope_arg() {
+  return (const RopeSpec*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + kBwdRopeArgOffset);
+}
+
 __device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
   BwdParams p;
   p.q = uni(in.q); p.k = uni(in.k); p.v = uni(in.v); p.o = uni(in.o); p.o_lo = uni(in.o_lo);
@@ -252,8 +260,8 @@ __device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
 // The whole dK/dV pass for one workgroup.  Kept out of line so that the rare variant for
 // key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
 // allocation instead of raising the common variant's.
-template <int DT, bool PRECISE>
-__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg_in) {
+template <int DT, bool PRECISE, bool ROPE>
+__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg_in, const RopeSpec* rope) {
   const BwdParams p = uniform_params(pin);
   const int wg = uni(wg_in);
   const int tid = threadIdx.x;
@@ -384,8 +392,9 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = db * 32 + 8 * r4 + 4 * W.hl;
-      const f32x4 kv = {W.dk[db][4 * r4] * p.scale, W.dk[db][4 * r4 + 1] * p.scale, W.dk[db][4 * r4 + 2] * p.scale,
-                        W.dk[db][4 * r4 + 3] * p.scale};
+      f32x4 kv = {W.dk[db][4 * r4] * p.scale, W.dk[db][4 * r4 + 1] * p.scale, W.dk[db][4 * r4 + 2] * p.scale,
+                  W.dk[db][4 * r4 + 3] * p.scale};
+      if constexpr (ROPE) kv = rope_back4(kv, j, *rope, d0 / 2);  // gradient of the unrotated K
       const f32x4 vv = {W.dv[db][4 * r4], W.dv[db][4 * r4 + 1], W.dv[db][4 * r4 + 2], W.dv[db][4 * r4 + 3]};
       *(f32x4*)(dkslab + (size_t)j * kHeadDim + d0) = kv;
       *(f32x4*)(dvslab + (size_t)j * kHeadDim + d0) = vv;
@@ -395,18 +404,18 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
 // Sink keys collect attention from every later query, so their dK and dV are sums of many
 // large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value plus
 // its rounded residual (two products each), which keeps their rounding out of the sum.
-template <int DT>
-__device__ __forceinline__ void dkdv_dispatch(const BwdParams& p, int wg) {
+template <int DT, bool ROPE>
+__device__ __forceinline__ void dkdv_dispatch(const BwdParams& p, int wg, const RopeSpec* rope) {
   const int kblk = wg / (p.B * p.G);
   if (p.mask.window > 0 && kblk * kDkdvKeys < p.mask.sinks)
-    dkdv_block<DT, true>(p, wg);
+    dkdv_block<DT, true, ROPE>(p, wg, rope);
   else
-    dkdv_block<DT, false>(p, wg);
+    dkdv_block<DT, false, ROPE>(p, wg, rope);
 }
 
-template <int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
-  dkdv_dispatch<DT>(p, (int)blockIdx.x);
+template <int DT, bool ROPE>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, RopeSpec) {
+  dkdv_dispatch<DT, ROPE>(p, (int)blockIdx.x, ROPE ? kernel_rope_arg() : nullptr);
 }
 
 // ------------------------------------------------------------------------------------
@@ -418,8 +427,8 @@ __shared__ __attribute__((aligned(1024))) char g_dq_k1[8192];
 __shared__ __attribute__((aligned(1024))) char g_dq_v0[8192];
 __shared__ __attribute__((aligned(1024))) char g_dq_v1[8192];
 
-template <int DT>
-__device__ __forceinline__ void dq_body(const BwdParams& p, int wg) {
+template <int DT, bool ROPE>
+__device__ __forceinline__ void dq_body(const BwdParams& p, int wg, const RopeSpec* rope) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -609,35 +618,50 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int wg) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = db * 32 + 8 * r4 + 4 * hl;
-        const f32x4 w = {dq[db][cb][4 * r4] * p.scale, dq[db][cb][4 * r4 + 1] * p.scale,
-                         dq[db][cb][4 * r4 + 2] * p.scale, dq[db][cb][4 * r4 + 3] * p.scale};
+        f32x4 w = {dq[db][cb][4 * r4] * p.scale, dq[db][cb][4 * r4 + 1] * p.scale,
+                   dq[db][cb][4 * r4 + 2] * p.scale, dq[db][cb][4 * r4 + 3] * p.scale};
+        if constexpr (ROPE) w = rope_back4(w, i, *rope, d0 / 2);  // gradient of the unrotated Q
         *(f32x4*)(p.dq + (qslab_rows + i) * kHeadDim + d0) = w;
       }
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  dq_body<DT>(p, (int)blockIdx.x);
+template <int DT, bool ROPE>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, RopeSpec) {
+  dq_body<DT, ROPE>(p, (int)blockIdx.x, ROPE ? kernel_rope_arg() : nullptr);
 }
 
-template <int DT>
-__device__ __attribute__((noinline)) void dq_block(const BwdParams& pin, int wg) {
-  dq_body<DT>(uniform_params(pin), uni(wg));
+template <int DT, bool ROPE>
+__device__ __attribute__((noinline)) void dq_block(const BwdParams& pin, int wg, const RopeSpec* rope) {
+  dq_body<DT, ROPE>(uniform_params(pin), uni(wg), rope);
 }
 
 // dK/dV and dQ in one launch: the dK/dV workgroups (heaviest key blocks first) come first,
 // then the dQ workgroups (heaviest query blocks first), so dQ work fills the CUs that the
 // light dK/dV blocks free while the heavy ones still run.  The two passes are independent
 // (both only read Q, K, V, dO, lse, delta) and each keeps its own register allocation.
-template <int DT>
-__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdParams p) {
+template <int DT, bool ROPE>
+__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdParams p, RopeSpec) {
   const int n_dkdv = p.n_kblk * p.B * p.G;
   const int wg = (int)blockIdx.x;
+  const RopeSpec* rope = ROPE ? kernel_rope_arg() : nullptr;
   if (wg < n_dkdv)
-    dkdv_dispatch<DT>(p, wg);
+    dkdv_dispatch<DT, ROPE>(p, wg, rope);
   else
-    dq_block<DT>(p, wg - n_dkdv);
+    dq_block<DT, ROPE>(p, wg - n_dkdv, rope);
+}
+
+// Kernels by element type and by whether dQ / dK are rotated back at the store.
+template <bool ROPE>
+const void* bwd_kernel(int which, int dtype) {
+  const bool bf = dtype == kDtBF16;
+  if (which == 0) return bf ? (const void*)bwd_dkdv_kernel<kDtBF16, ROPE> : (const void*)bwd_dkdv_kernel<kDtF16, ROPE>;
+  if (which == 1) return bf ? (const void*)bwd_dq_kernel<kDtBF16, ROPE> : (const void*)bwd_dq_kernel<kDtF16, ROPE>;
+  return bf ? (const void*)bwd_fused_kernel<kDtBF16, ROPE> : (const void*)bwd_fused_kernel<kDtF16, ROPE>;
+}
+
+const void* pick_bwd(int which, const RopeSpec& rope, int dtype) {
+  return rope.enabled ? bwd_kernel<true>(which, dtype) : bwd_kernel<false>(which, dtype);
 }
 
 }  // namespace
@@ -654,26 +678,23 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s) {
   }
 }
 
-hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s) {
+hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(256);
-  void* args[] = {(void*)&p};
-  if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtBF16>, grid, block, args, 0, s);
-  return hipLaunchKernel((const void*)bwd_dkdv_kernel<kDtF16>, grid, block, args, 0, s);
+  void* args[] = {(void*)&p, (void*)&rope};
+  return hipLaunchKernel(pick_bwd(0, rope, dtype), grid, block, args, 0, s);
 }
 
-hipError_t launch_bwd_dq_mfma(const BwdParams& p, int dtype, hipStream_t s) {
+hipError_t launch_bwd_dq_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   dim3 grid((unsigned)((long long)p.n_qblk * p.B * (p.H / p.hpw))), block(256);
-  void* args[] = {(void*)&p};
-  if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_dq_kernel<kDtBF16>, grid, block, args, 0, s);
-  return hipLaunchKernel((const void*)bwd_dq_kernel<kDtF16>, grid, block, args, 0, s);
+  void* args[] = {(void*)&p, (void*)&rope};
+  return hipLaunchKernel(pick_bwd(1, rope, dtype), grid, block, args, 0, s);
 }
 
-hipError_t launch_bwd_fused_mfma(const BwdParams& p, int dtype, hipStream_t s) {
+hipError_t launch_bwd_fused_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   const long long n = (long long)p.n_kblk * p.B * p.G + (long long)p.n_qblk * p.B * (p.H / p.hpw);
   dim3 grid((unsigned)n), block(256);
-  void* args[] = {(void*)&p};
-  if (dtype == kDtBF16) return hipLaunchKernel((const void*)bwd_fused_kernel<kDtBF16>, grid, block, args, 0, s);
-  return hipLaunchKernel((const void*)bwd_fused_kernel<kDtF16>, grid, block, args, 0, s);
+  void* args[] = {(void*)&p, (void*)&rope};
+  return hipLaunchKernel(pick_bwd(2, rope, dtype), grid, block, args, 0, s);
 }
 
 }  // namespace gqa

@@ -263,4 +263,54 @@ __device__ __forceinline__ void unit_store_rm_flip(char* tile, const Unit& u, in
 // Row of the accumulator register r of this lane, inside a 32-row block.
 __device__ __forceinline__ int acc_row(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
 
+// ---- rotary position embedding ----
+// m cos and m sin of the angle of a dimension pair at position pos, for a pair turning rev
+// revolutions per position: pos * rev is formed in fp64 (within an fp64 ulp for any int
+// position) and its whole revolutions dropped there, so the fp32 sine and cosine of
+// pi * (2 f), f in [-1/2, 1/2], see an angle accurate to fp32 rounding at any position.
+// R^T (the backward) flips the sine.
+__device__ __forceinline__ void rope_cs(int pos, double rev, float mscale, bool inverse, float& mc, float& ms) {
+  const double t = (double)pos * rev;
+  const float f2 = (float)(2.0 * (t - __builtin_rint(t)));
+  float s, c;
+  sincospif(f2, &s, &c);
+  mc = mscale * c;
+  ms = inverse ? -(mscale * s) : mscale * s;
+}
+
+// The pair (x0, x1) rotated by the angle whose m cos and m sin are mc and ms.
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, float mc, float ms) {
+  const float y0 = __builtin_fmaf(x0, mc, -(x1 * ms));
+  const float y1 = __builtin_fmaf(x0, ms, x1 * mc);
+  x0 = y0;
+  x1 = y1;
+}
+
+// Rotate back (m R^T at position pos) the two pairs held in 4 consecutive fp32 gradient
+// values that start at pair index pi.
+__device__ __forceinline__ f32x4 rope_back4(f32x4 v, int pos, const RopeSpec& r, int pi) {
+  float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  float mc, ms;
+  rope_cs(pos, r.rev[pi], r.mscale, true, mc, ms);
+  rope_pair(x0, x1, mc, ms);
+  rope_cs(pos, r.rev[pi + 1], r.mscale, true, mc, ms);
+  rope_pair(x2, x3, mc, ms);
+  return f32x4{x0, x1, x2, x3};
+}
+
+// Rotate the 4 pairs packed in w (8 16-bit elements) at position pos; rev[j] is the
+// frequency of the j-th pair.
+template <int DT>
+__device__ __forceinline__ u32x4 rope_chunk16(u32x4 w, int pos, const double (&rev)[4], float mscale, bool inverse) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float mc, ms;
+    rope_cs(pos, rev[j], mscale, inverse, mc, ms);
+    float x0 = elem_to_f32<DT>(w[j], 0), x1 = elem_to_f32<DT>(w[j], 1);
+    rope_pair(x0, x1, mc, ms);
+    w[j] = pack2<DT>(x0, x1);
+  }
+  return w;
+}
+
 }  // namespace gqa

@@ -14,6 +14,7 @@ namespace {
 constexpr int kPad = kHeadDim + 1;  // LDS row pitch in floats (avoids bank conflicts)
 
 // One wave per (b, h, 64-row tile); lane = query row.
+template <bool ROPE>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   __shared__ float ks[kTile][kPad];
   __shared__ float vs[kTile][kPad];
@@ -33,9 +34,24 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   float q[kHeadDim], acc[kHeadDim];
 #pragma unroll
   for (int c = 0; c < kHeadDim; ++c) {
-    q[c] = row_ok ? qrow[c] * p.scale : 0.f;
+    q[c] = row_ok ? qrow[c] : 0.f;
     acc[c] = 0.f;
   }
+  if constexpr (ROPE) {  // rotary embedding of the lane's query row, at position i
+#pragma unroll
+    for (int j = 0; j < kRopePairs; ++j) {
+      float mc, ms;
+      rope_cs(i, p.rope.rev[j], p.rope.mscale, false, mc, ms);
+      rope_pair(q[2 * j], q[2 * j + 1], mc, ms);
+    }
+    if (p.q_rot != nullptr && row_ok) {
+      float* rrow = (float*)p.q_rot + ((size_t)bh * S + i) * kHeadDim;
+#pragma unroll
+      for (int c = 0; c < kHeadDim; ++c) rrow[c] = q[c];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kHeadDim; ++c) q[c] *= p.scale;
   float mx = -INFINITY, l = 0.f;
 
   const TileRanges tr = key_tiles_for_rows(m, qt * kTile, imin(qt * kTile + kTile - 1, S - 1));
@@ -215,7 +231,8 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdParams p) {
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s) {
   const long long n = (long long)p.B * p.H * ((p.S + kTile - 1) / kTile);
   void* args[] = {(void*)&p};
-  return hipLaunchKernel((const void*)fwd_f32_kernel, dim3((unsigned)n), dim3(64), args, 0, s);
+  const void* fn = p.rope.enabled ? (const void*)fwd_f32_kernel<true> : (const void*)fwd_f32_kernel<false>;
+  return hipLaunchKernel(fn, dim3((unsigned)n), dim3(64), args, 0, s);
 }
 
 hipError_t launch_bwd_dkdv_f32(const BwdParams& p, hipStream_t s) {

@@ -262,7 +262,7 @@ __device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t rs, char* tile
                                              row0 * 128 + voff[u], 0, 0, 0);
 }
 
-template <int DT>
+template <int DT, bool ROPE>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_lds0[8192];
   __shared__ __attribute__((aligned(1024))) char k_lds1[8192];
@@ -314,6 +314,24 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       W.qf[cb][ks] = buf_load16(qrs, (W.q0 + cb * 32 + W.l32) * 128 + ks * 32 + W.hl * 16);
+  if constexpr (ROPE) {
+    // Rotary embedding of the wave's Q tile in registers: this lane holds pairs
+    // 8 ks + 4 hl .. + 3 of rows q0 + cb * 32 + l32 (rows past S are zeros and stay so).
+    const __amdgpu_buffer_rsrc_t qrot =
+        slab_rsrc((const uint16_t*)p.q_rot + (size_t)(b * p.H + h) * S * kHeadDim, S);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        double rev[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rev[j] = W.hl ? p.rope.rev[8 * ks + 4 + j] : p.rope.rev[8 * ks + j];
+        const int row = W.q0 + cb * 32 + W.l32;
+        W.qf[cb][ks] = rope_chunk16<DT>(W.qf[cb][ks], row, rev, p.rope.mscale, false);
+        if (p.q_rot != nullptr)  // stores past the slab's end are dropped
+          __builtin_amdgcn_raw_buffer_store_b128(W.qf[cb][ks], qrot, row * 128 + ks * 32 + W.hl * 16, 0, 0);
+      }
+  }
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -411,8 +429,12 @@ hipError_t launch_fwd_mfma(const FwdParams& p, int dtype, hipStream_t s) {
   const long long nblk = (long long)p.n_qblk * p.B * (p.H / p.hpw);
   dim3 grid((unsigned)nblk), block(256);
   void* args[] = {(void*)&p};
-  if (dtype == kDtBF16) return hipLaunchKernel((const void*)fwd_mfma_kernel<kDtBF16>, grid, block, args, 0, s);
-  return hipLaunchKernel((const void*)fwd_mfma_kernel<kDtF16>, grid, block, args, 0, s);
+  const void* fn;
+  if (p.rope.enabled)
+    fn = dtype == kDtBF16 ? (const void*)fwd_mfma_kernel<kDtBF16, true> : (const void*)fwd_mfma_kernel<kDtF16, true>;
+  else
+    fn = dtype == kDtBF16 ? (const void*)fwd_mfma_kernel<kDtBF16, false> : (const void*)fwd_mfma_kernel<kDtF16, false>;
+  return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
 }  // namespace gqa

@@ -119,6 +119,17 @@ __host__ __device__ inline TileRanges query_tiles_for_keys(const MaskSpec& m, in
 // ---------------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value).
 // ---------------------------------------------------------------------------------
+
+// Rotary position embedding with YaRN frequencies, as the kernels take it: the per-pair
+// frequencies are worked out on the host from the configuration (like the softmax scale);
+// the angles of each position and the rotations run on the device.
+constexpr int kRopePairs = kHeadDim / 2;
+struct RopeSpec {
+  double rev[kRopePairs];  // pair i turns rev[i] revolutions per position (theta'_i / 2 pi)
+  float mscale;            // factor on each rotated vector (YaRN's attention temperature)
+  int enabled;             // forward: rotate Q in registers before the scores
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -133,6 +144,21 @@ struct FwdParams {
   int hpw;           // heads per workgroup (a divisor of H/G): waves 0..hpw-1 share rows
   int qpw;           // 64-row query tiles per workgroup (4 / hpw)
   int n_qblk;        // workgroup row blocks per head = ceil(S / (64 * qpw))
+  void* q_rot;       // with rope.enabled: optional output of the rotated Q (element type)
+  RopeSpec rope;     // query i sits at position i
+};
+
+// y = mscale R(pos0 + s) x (R^T with inverse) for the rows s of x, y [n_slabs][S][64].
+struct RopeParams {
+  const void* x;
+  void* y;           // == x (in place) or disjoint
+  long long n_slabs;
+  int S;
+  int pos0;          // pos0 + S - 1 fits in int
+  int slabs_per_block;
+  int n_row_blocks;  // ceil(S / rows per block)
+  int inverse;
+  RopeSpec spec;
 };
 
 struct BwdParams {
@@ -155,6 +181,11 @@ struct BwdParams {
   int hpw, qpw, n_qblk;  // dQ pass: same row decomposition as the forward
   int n_kblk;            // dK/dV pass: kDkdvKeys-key blocks per kv head
 };
+
+// The dK/dV and dQ kernels take (BwdParams, RopeSpec); with rope.enabled they rotate dQ and
+// dK back (m R^T at their positions) as they store them.  The second argument starts at
+// this offset of the kernel-argument segment (arguments in order, each at its alignment).
+constexpr size_t kBwdRopeArgOffset = (sizeof(BwdParams) + alignof(RopeSpec) - 1) / alignof(RopeSpec) * alignof(RopeSpec);
 
 // Launchers (return hipSuccess or the launch error).  Element type by dtype code.
 // Decode (few query rows against a key/value cache), split over the visible key tiles.
@@ -188,12 +219,15 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
 
+hipError_t launch_rope(const RopeParams& p, int dtype, hipStream_t s);
+int rope_rows_per_block(int dtype);
+
 hipError_t launch_fwd_mfma(const FwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s);
-hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, int dtype, hipStream_t s);
-hipError_t launch_bwd_dq_mfma(const BwdParams& p, int dtype, hipStream_t s);
-hipError_t launch_bwd_fused_mfma(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s);
+hipError_t launch_bwd_fused_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdParams& p, hipStream_t s);
 
