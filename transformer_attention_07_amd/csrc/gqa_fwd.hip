@@ -317,8 +317,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   if constexpr (ROPE) {
     // Rotary embedding of the wave's Q tile in registers: this lane holds pairs
     // 8 ks + 4 hl .. + 3 of rows q0 + cb * 32 + l32 (rows past S are zeros and stay so).
-    const __amdgpu_buffer_rsrc_t qrot =
-        slab_rsrc((const uint16_t*)p.q_rot + (size_t)(b * p.H + h) * S * kHeadDim, S);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -326,10 +324,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         double rev[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) rev[j] = W.hl ? p.rope.rev[8 * ks + 4 + j] : p.rope.rev[8 * ks + j];
-        const int row = W.q0 + cb * 32 + W.l32;
-        W.qf[cb][ks] = rope_chunk16<DT>(W.qf[cb][ks], row, rev, p.rope.mscale, false);
-        if (p.q_rot != nullptr)  // stores past the slab's end are dropped
-          __builtin_amdgcn_raw_buffer_store_b128(W.qf[cb][ks], qrot, row * 128 + ks * 32 + W.hl * 16, 0, 0);
+        W.qf[cb][ks] = rope_chunk16<DT>(W.qf[cb][ks], W.q0 + cb * 32 + W.l32, rev, p.rope.mscale, false);
       }
   }
 #pragma unroll
@@ -395,6 +390,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     tile(std::integral_constant<int, 2>{}, n + 2);
   }
 
+  if constexpr (ROPE) {
+    // the rotated Q tile for the backward, stored once the tile loop is done so that these
+    // writes spread over the run instead of joining every workgroup's first loads
+    if (p.q_rot != nullptr) {
+      const __amdgpu_buffer_rsrc_t qrot =
+          slab_rsrc((const uint16_t*)p.q_rot + (size_t)(b * p.H + h) * S * kHeadDim, S);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)  // stores past the slab's end are dropped
+          __builtin_amdgcn_raw_buffer_store_b128(W.qf[cb][ks], qrot,
+                                                 (W.q0 + cb * 32 + W.l32) * 128 + ks * 32 + W.hl * 16, 0, 0);
+    }
+  }
   if (!active) return;
   uint16_t* oslab = (uint16_t*)p.o + (size_t)(b * p.H + h) * S * kHeadDim;
   uint16_t* olo_slab = p.o_lo ? (uint16_t*)p.o_lo + (size_t)(b * p.H + h) * S * kHeadDim : nullptr;
