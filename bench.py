@@ -14,8 +14,9 @@ carries the step throughput, a roofline record for the dominant kernel (timed
 with HIP events on the stream the kernels run on) and the CPU fp64 oracle
 timed on a bounded sample of the same work on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50]
-                       [--workload step|c2|c3|c4|c5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--rope]
+                       [--workload step|c2|c3|c4|c5|long|decode|decode16|rope_k]
+                       [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -47,7 +48,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="step",
-                    choices=["step", "c2", "c3", "c4", "c5", "long", "decode", "decode16"])
+                    choices=["step", "c2", "c3", "c4", "c5", "long", "decode", "decode16", "rope_k"])
     ap.add_argument("--rope", action="store_true",
                     help="YaRN RoPE (factor 32) on q and k in front of attention: rotation of K, the "
                          "forward with Q rotated in registers, and dQ / dK rotated back after the backward")
@@ -291,6 +292,70 @@ def run_decode(args, w):
     print(json.dumps(line), flush=True)
 
 
+def run_rope_k(args):
+    """The rotation kernel alone, on the model card's long-context K shape
+    [2][16][204800][64] bf16 at positions 0 .. 204,799: each call reads and writes every
+    element once (HBM-bound)."""
+    import torch
+
+    import transformer_attention_07_amd as gqa
+
+    B, G, S, D = 2, 16, 204800, 64
+    print(f"[bench] rotation of K [{B}][{G}][{S}][{D}] bf16", file=sys.stderr, flush=True)
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(1250)
+    x = torch.randn(B, G, S, D, generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        gqa.gqa_rope_apply(x, out=y, stream=stream)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        gqa.gqa_rope_apply(x, out=y, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_call = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    nbytes = 2.0 * x.numel() * x.element_size()
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    ach = nbytes / (ms_call * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.rope as ref
+        from threadpoolctl import threadpool_info
+
+        print("[bench] timing the CPU oracle on one slab", file=sys.stderr, flush=True)
+        xs = x[0, 0].cpu()
+        t1 = time.perf_counter()
+        ref.rope(xs, list(range(S)))
+        dt = time.perf_counter() - t1
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        cpu = {"value": 2.0 * xs.numel() * 2 / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"one [{S}][{D}] slab of {B * G}, {dt:.1f} s, fp64 numpy"}
+    line = {
+        "metric": "YaRN rotary embedding HBM throughput (algorithmic bytes / time)", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic N(0,1), seeded",
+        "config": {"workload": f"YaRN RoPE (factor 32) of K [{B}][{G}][{S}][{D}] bf16, positions 0..{S - 1}",
+                   "bytes_per_step": nbytes, "rope": dict(gqa.YARN_ROPE), "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels": {"rope": {"ms": round(ms_call, 5), "gbs": round(ach, 1)}},
+        "roofline": {"bound": "hbm", "kernel": "rope", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic("rope", "rope_k")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -298,14 +363,26 @@ def main():
               "single MI355X (no collectives, no sharding); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.reduce_counters:
-        reduce_counters(*args.reduce_counters,
-                        args.workload if args.workload.startswith("decode") else workload(args.workload).name)
+        special = args.workload.startswith("decode") or args.workload == "rope_k"
+        name = args.workload if special else workload(args.workload).name + ("_rope" if args.rope else "")
+        reduce_counters(*args.reduce_counters, name)
         return
     long_step = args.workload == "long"
     if args.steps is None:
         args.steps = 3 if long_step else 100
     if args.warmup is None:
         args.warmup = 1 if long_step else 50
+    if args.workload == "rope_k":
+        import torch
+
+        import transformer_attention_07_amd as gqa
+
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        gqa.library()
+        run_rope_k(args)
+        return
     if args.workload.startswith("decode"):
         import torch
 
