@@ -14,7 +14,7 @@ carries the step throughput, a roofline record for the dominant kernel (timed
 with HIP events on the stream the kernels run on) and the CPU fp64 oracle
 timed on a bounded sample of the same work on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--rope]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--rope | --fp8]
                        [--workload step|c2|c3|c4|c5|long|decode|decode16|rope_k]
                        [--no-cpu-baseline]
 """
@@ -33,10 +33,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PFLOP/s dense)
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # twice the bf16 rate (published 5.0 PFLOP/s dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal GQA attention TFLOP/s (fwd, bwd) at d=64 + % of MI355X bf16 MFMA peak"
-KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_device.h",
-                  "gqa_internal.h"]
+KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_fwd_fp8.hip",
+                  "gqa_device.h", "gqa_internal.h"]
 
 
 def parse_args():
@@ -52,6 +53,8 @@ def parse_args():
     ap.add_argument("--rope", action="store_true",
                     help="YaRN RoPE (factor 32) on q and k in front of attention: rotation of K, the "
                          "forward with Q rotated in registers, and dQ / dK rotated back after the backward")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward only, with FP8 (e4m3) Q, K, V and per-tensor scales, on the FP8 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -97,7 +100,8 @@ def load_traffic(kernel, wname):
     return ent.get("bytes_per_launch")
 
 
-KERNEL_KEYS = {"rope_kernel": "rope", "fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
+KERNEL_KEYS = {"rope_kernel": "rope", "fwd_fp8_kernel": "fwd_fp8", "vt_permute_kernel": "vt_permute",
+               "fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
                "bwd_fused_kernel": "bwd_grads", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq",
                "decode_split_kernel": "decode", "decode_merge_kernel": "decode_merge", "copyBuffer": "copy"}
 COPY_BYTES = 1 << 30
@@ -356,6 +360,74 @@ def run_rope_k(args):
     print(json.dumps(line), flush=True)
 
 
+def run_fp8(args, w):
+    """The FP8 forward on a forward workload: e4m3 Q, K, V with per-tensor scales; one call
+    = the V^T permute pre-pass + the forward kernel."""
+    import torch
+
+    import transformer_attention_07_amd as gqa
+    from synth import make_fp8_inputs
+
+    print(f"[bench] fp8 workload {w}", file=sys.stderr, flush=True)
+    q8, k8, v8, sc = make_fp8_inputs(w)
+    dev = torch.device("cuda", 0)
+    q8d, k8d, v8d = q8.to(dev), k8.to(dev), v8.to(dev)
+    kw = dict(causal=w.causal, window=w.window, num_sinks=w.num_sinks, scale=w.scale)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, gqa.gqa_attn_fwd_fp8_workspace_bytes(q8d, k8d, w.causal, w.window, w.num_sinks)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        gqa.gqa_attn_fwd_fp8(q8d, k8d, v8d, *sc, out=o, lse=lse, workspace=ws, stream=stream, **kw)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_call = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
+    flop = 4.0 * w.D * pairs * w.B * w.H
+    value = flop / (ms_step * 1e-3) / 1e12
+    ach = flop / (ms_call * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        deq = tuple(x.to(torch.float32) * s for x, s in zip((q8, k8, v8), sc)) + (None,)
+        cpu = cpu_baseline(w, deq, args.cpu_seconds)
+    wl = (f"causal GQA fwd, FP8 e4m3 Q/K/V (per-tensor scales) and P, B={w.B} H={w.H} G={w.G} S={w.S} d={w.D}"
+          + (f" window={w.window} sinks={w.num_sinks}" if w.window else "") + ", O bf16")
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3", "data": "synthetic N(0,1) quantised per tensor, seeded",
+        "config": {"workload": wl, "B": w.B, "H": w.H, "G": w.G, "S": w.S, "D": w.D, "causal": w.causal,
+                   "window": w.window, "num_sinks": w.num_sinks, "visible_pairs_per_head": pairs,
+                   "flop_per_step": flop, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / MFMA_FP8_PEAK_TFLOPS, 2),
+        "pct_of_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernels": {"fwd_fp8": {"ms": round(ms_call, 5), "tflops": round(ach, 1)}},
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8 (V^T permute + forward, one call)", "achieved": round(ach, 2),
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic("fwd_fp8", w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -406,6 +478,12 @@ def main():
         sys.exit(1)
     gqa.library()  # fail loudly if the HIP library is not built
     w = workload(args.workload)
+    if args.fp8:
+        if args.rope or "bwd" in w.direction:
+            print("--fp8 is a forward-only mode without --rope (workloads c2, c3, c4)", file=sys.stderr)
+            sys.exit(2)
+        run_fp8(args, w.with_(name=w.name + "_fp8"))
+        return
     if args.rope:
         w = w.with_(name=w.name + "_rope")
     do_bwd = "bwd" in w.direction

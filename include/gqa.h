@@ -248,6 +248,29 @@ int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot
                       const void* v, const void* o, const void* o_lo, const float* lse, const void* d_o,
                       float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * FP8 forward: the forward above with Q, K and V in FP8 (OCP e4m3, one byte per element)
+ * and per-tensor dequantisation factors -- the "FP8 computation" of the model card's
+ * FlashAttention-3 forward (Protected Inventions list).  Both products run on the FP8
+ * matrix cores: S = scale * (q_scale Q8)(k_scale K8)^T, P = softmax, and O = P (v_scale V8)
+ * with P rounded to e4m3 for the second product; row sums, lse and accumulation in fp32.
+ *
+ * Layout: Q8 [B][H][S][D], K8 and V8 [B][G][S][D] (e4m3 bytes); O [B][H][S][D] in
+ * p->dtype, which must be GQA_BF16; lse [B][H][S] fp32 (natural log of the scaled scores).
+ * The workspace (gqa_attn_fwd_fp8_workspace_bytes) receives V transposed per kv head, in
+ * the key order the kernel's operands need; its contents need no initialisation.
+ * Errors as gqa_attn_fwd, plus GQA_ERR_INVALID_ARG for a missing or non-positive scale,
+ * GQA_ERR_WORKSPACE for a missing or short workspace, GQA_ERR_UNSUPPORTED for an output
+ * dtype other than GQA_BF16 or S > 2^24. */
+typedef struct gqa_fp8_scales {
+  float q, k, v; /* element value = scale * e4m3 code value; finite and > 0 */
+} gqa_fp8_scales;
+
+size_t gqa_attn_fwd_fp8_workspace_bytes(const gqa_problem* p);
+
+int gqa_attn_fwd_fp8(const gqa_problem* p, const gqa_fp8_scales* scales, const void* q8, const void* k8,
+                     const void* v8, void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

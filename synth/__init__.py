@@ -26,8 +26,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "sample_rows", "sample_rows_c4", "sample_rows_long",
-           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_fp8_inputs", "sample_rows", "sample_rows_c4",
+           "sample_rows_long", "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -95,6 +95,23 @@ def make_inputs(w: Workload, with_do: bool | None = None, seed: int | None = Non
         t = torch.randn(shp, generator=gen, dtype=torch.float32)
         out.append(t.to(w.torch_dtype).contiguous())
     return tuple(out)
+
+
+def make_fp8_inputs(w: Workload, seed: int | None = None):
+    """FP8 inputs of a workload: the same fp32 N(0, 1) draws as ``make_inputs`` (Q, K, V),
+    each divided by its own scale max|x| / 448 and rounded to OCP e4m3 (nearest even) by
+    PyTorch's conversion.  Returns CPU tensors (q8, k8, v8) of torch.float8_e4m3fn and the
+    scales (sq, sk, sv): element value = scale * code value."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    shapes = [(w.B, w.H, w.S, w.D), (w.B, w.G, w.S, w.D), (w.B, w.G, w.S, w.D)]
+    out, scales = [], []
+    for shp in shapes:
+        t = torch.randn(shp, generator=gen, dtype=torch.float32)
+        sc = float(t.abs().max()) / 448.0 if t.numel() else 1.0
+        out.append((t / sc).to(torch.float8_e4m3fn).contiguous())
+        scales.append(sc)
+    return out[0], out[1], out[2], tuple(scales)
 
 
 def _make_inputs_per_slab(w: Workload, with_do: bool, base: int):

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 15, declared
+    assert len(declared) == 17, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -254,3 +254,31 @@ def test_fwd_bwd_rope_argument_checks():
     assert lib.gqa_attn_bwd_rope(*args, None, need, None) == binding.GQA_ERR_WORKSPACE
     assert lib.gqa_attn_bwd_rope(*args, FAKE, need - 1, None) == binding.GQA_ERR_WORKSPACE
     assert lib.gqa_attn_bwd_rope(ctypes.byref(e), ctypes.byref(r), *([None] * 10), None, 0, None) == binding.GQA_OK
+
+
+# ---- FP8 forward: validation only (no launch) ----
+def test_fp8_forward_argument_checks():
+    lib = gqa.library()
+    p = gqa.make_problem(1, 4, 2, 128)
+    need = lib.gqa_attn_fwd_fp8_workspace_bytes(ctypes.byref(p))
+    assert need == ((1 * 2 * 64 * 128 + 255) // 256) * 256
+    ragged = gqa.make_problem(2, 8, 2, 100)
+    assert lib.gqa_attn_fwd_fp8_workspace_bytes(ctypes.byref(ragged)) == ((2 * 2 * 64 * 128 + 255) // 256) * 256
+    ok = binding.gqa_fp8_scales(0.01, 0.02, 0.03)
+
+    def call(p=p, sc=ok, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.gqa_attn_fwd_fp8(ctypes.byref(p), None if sc is None else ctypes.byref(sc), q, k, v, o, lse, ws,
+                                    wsb, None)
+    I = binding.GQA_ERR_INVALID_ARG
+    assert call(sc=None) == I
+    assert call(sc=binding.gqa_fp8_scales(0.0, 1.0, 1.0)) == I
+    assert call(sc=binding.gqa_fp8_scales(1.0, float("nan"), 1.0)) == I
+    assert call(sc=binding.gqa_fp8_scales(1.0, 1.0, -2.0)) == I
+    assert call(q=None) == I
+    assert call(o=FAKE + 8) == I
+    assert call(ws=None, wsb=need) == binding.GQA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == binding.GQA_ERR_WORKSPACE
+    assert call(p=gqa.make_problem(1, 4, 2, 128, dtype=binding.GQA_F16)) == binding.GQA_ERR_UNSUPPORTED
+    assert call(p=gqa.make_problem(1, 4, 2, 128, D=128)) == binding.GQA_ERR_UNSUPPORTED
+    e = gqa.make_problem(0, 4, 2, 128)
+    assert call(p=e, q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0) == binding.GQA_OK

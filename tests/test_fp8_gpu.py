@@ -1,0 +1,153 @@
+"""FP8 forward (gqa_attn_fwd_fp8, through the C-ABI) against the CPU fp64 oracle.
+
+The inputs are e4m3 codes with per-tensor scales (synth.make_fp8_inputs); the oracle is
+the plain attention (oracle.attention) over the dequantised values, which are exact in
+fp64, so every difference comes from the kernel's own roundings.  The one that matters is
+P rounded to e4m3 for the P V product; the bounds derive from it:
+  * per element, with p the oracle's probabilities of the row and p_max their maximum:
+        |O - O*| <= sum_j max(2^-4 p_j, 2^-10 p_max) |v_jc| + 2^-9 |O*| + 1e-4
+    (an e4m3 value within half an ulp: 2^-4 relative for normal values, 2^-10 absolute
+    below 2^-6, relative to the row maximum -- a running maximum below the true one only
+    scales P up, which does not loosen this; 2^-9 for O's bf16 rounding; 1e-4 for fp32
+    arithmetic);
+  * on average, treating each P rounding as an independent error uniform within its half
+    ulp hu_j: mean |O - O*| <= mean(2 sqrt(2/pi) sigma + 2^-9 |O*|),
+    sigma^2 = sum_j hu_j^2 v_jc^2 / 3 (twice the expected size, plus O's rounding);
+  * lse (from fp32 row sums of the unrounded P and fp32 scores of exact products):
+    1e-3 max abs, as the bf16 path.
+Small cases are compared in full; the card's head layout at S = 16,384 (and the window +
+sink workload) on sampled rows.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as ref
+import transformer_attention_07_amd as gqa
+from synth import WORKLOADS, Workload, make_fp8_inputs, sample_rows, sample_rows_c4
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX = 1e-3
+
+
+def _slab(x8, sc, b, h):
+    return x8[b, h].to(torch.float32).numpy().astype(np.float64) * sc
+
+
+def _bounds(q8, k8, v8, sc, b, h, rows, w):
+    """Oracle O, lse for the rows of head (b, h) over the dequantised inputs, and the
+    rows' per-element and mean error bounds."""
+    H, G = q8.shape[1], k8.shape[1]
+    g = h // (H // G)
+    kk, vv = _slab(k8, sc[1], b, g), _slab(v8, sc[2], b, g)
+    qr = q8[b, h].to(torch.float32).numpy()[rows].astype(np.float64) * sc[0]
+    s = ref._scores(qr, kk, rows, w.scale, w.causal, w.window, w.num_sinks)
+    p, lse = ref._softmax_rows(s)
+    O = p @ vv
+    hu = np.maximum(2.0 ** -4 * p, 2.0 ** -10 * p.max(axis=1, keepdims=True))
+    tol = hu @ np.abs(vv) + 2.0 ** -9 * np.abs(O) + 1e-4
+    mean_bound = 2.0 * np.sqrt(2.0 / np.pi) * np.sqrt((hu ** 2) @ (vv ** 2) / 3.0) + 2.0 ** -9 * np.abs(O)
+    return O, lse, tol, mean_bound
+
+
+def _check_rows(w, rows_bhi, q8, k8, v8, sc, o, lse):
+    got_o, got_l, want_o, want_l, tols, mb = [], [], [], [], [], []
+    trip = np.asarray(rows_bhi)
+    for (b, h) in sorted(set(map(tuple, trip[:, :2].tolist()))):
+        sel = trip[(trip[:, 0] == b) & (trip[:, 1] == h), 2]
+        O, L, tol, m = _bounds(q8, k8, v8, sc, b, h, sel, w)
+        want_o.append(O)
+        want_l.append(L)
+        tols.append(tol)
+        mb.append(m)
+        idx = torch.as_tensor(sel, device=o.device)
+        got_o.append(o[b, h].index_select(0, idx).double().cpu().numpy())
+        got_l.append(lse[b, h].index_select(0, idx).double().cpu().numpy())
+    go, wo, tol, mb = (np.concatenate(x) for x in (got_o, want_o, tols, mb))
+    err = np.abs(go - wo)
+    el = np.abs(np.concatenate(got_l) - np.concatenate(want_l))
+    print(f"  {len(trip)} rows: O max {err.max():.3e} mean {err.mean():.3e} (worst err/bound {(err / tol).max():.3f}; "
+          f"mean bound {mb.mean():.3e}); lse max {el.max():.3e}", flush=True)
+    assert np.isfinite(err).all() and np.isfinite(el).all()
+    assert (err <= tol).all(), f"{int((err > tol).sum())} elements beyond the e4m3 bound"
+    assert err.mean() <= mb.mean(), f"mean error {err.mean():.3e} > {mb.mean():.3e}"
+    assert el.max() <= LSE_MAX
+
+
+def _run(w, q8, k8, v8, sc):
+    o, lse = gqa.gqa_attn_fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *sc, causal=w.causal, window=w.window,
+                                  num_sinks=w.num_sinks, scale=w.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SMALL = [
+    # (B, H, G, S, causal, window, sinks)
+    (1, 4, 2, 1, True, 0, 0),
+    (1, 4, 2, 65, True, 0, 0),
+    (2, 8, 2, 200, True, 0, 0),
+    (1, 8, 8, 130, True, 0, 0),
+    (1, 6, 2, 257, True, 0, 0),
+    (1, 4, 1, 190, True, 0, 0),
+    (1, 4, 2, 300, False, 0, 0),
+    (1, 8, 2, 700, True, 100, 50),
+    (1, 8, 2, 640, True, 64, 64),
+    (1, 4, 2, 520, True, 1, 3),
+    (1, 16, 2, 1100, True, 300, 130),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}G{}S{}c{}W{}N{}".format(*c))
+def test_fp8_small_full(case):
+    B, H, G, S, causal, W, NS = case
+    w = Workload("fp8_small", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, seed=7100 + S + H)
+    print(f"[fp8] {w}", flush=True)
+    q8, k8, v8, sc = make_fp8_inputs(w)
+    o, lse = _run(w, q8, k8, v8, sc)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S)])
+    _check_rows(w, rows, q8, k8, v8, sc, o, lse)
+
+
+def test_fp8_large_dynamic_range_scales():
+    # scales far from 1 (tiny and huge codes-to-value factors) enter only through the
+    # softmax scale and the output scale
+    w = Workload("fp8_scales", B=1, H=8, G=2, S=333, window=90, num_sinks=20, seed=7200)
+    q8, k8, v8, _ = make_fp8_inputs(w)
+    sc = (3.0e-4, 5.0e-3, 40.0)
+    o, lse = _run(w, q8, k8, v8, sc)
+    rows = np.array([(0, h, i) for h in range(8) for i in range(333)])
+    _check_rows(w, rows, q8, k8, v8, sc, o, lse)
+
+
+@pytest.mark.timeout(600)
+def test_fp8_card_head_layout_sampled_rows():
+    w = WORKLOADS["c3"]
+    print(f"[fp8] {w}", flush=True)
+    q8, k8, v8, sc = make_fp8_inputs(w)
+    o, lse = _run(w, q8, k8, v8, sc)
+    rows = sample_rows(w.B, w.H, w.S, 512, w.seed, forced_rows=(0, 1, 63, 64, 8191, 16383))
+    _check_rows(w, rows, q8, k8, v8, sc, o, lse)
+
+
+@pytest.mark.timeout(600)
+def test_fp8_window_sinks_sampled_rows():
+    w = WORKLOADS["c4"]
+    print(f"[fp8] {w}", flush=True)
+    q8, k8, v8, sc = make_fp8_inputs(w)
+    o, lse = _run(w, q8, k8, v8, sc)
+    _check_rows(w, sample_rows_c4(w, n=512), q8, k8, v8, sc, o, lse)
+
+
+def test_fp8_is_deterministic_and_reuses_workspace():
+    w = Workload("fp8_det", B=2, H=8, G=2, S=500, window=128, num_sinks=16, seed=7300)
+    q8, k8, v8, sc = (t.cuda() if torch.is_tensor(t) else t for t in make_fp8_inputs(w))
+    ws = torch.full((gqa.gqa_attn_fwd_fp8_workspace_bytes(q8, k8, window=w.window, num_sinks=w.num_sinks),), 255,
+                    dtype=torch.uint8, device="cuda")
+    o1, l1 = gqa.gqa_attn_fwd_fp8(q8, k8, v8, *sc, window=w.window, num_sinks=w.num_sinks, workspace=ws)
+    o2, l2 = gqa.gqa_attn_fwd_fp8(q8, k8, v8, *sc, window=w.window, num_sinks=w.num_sinks, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -27,7 +27,7 @@ EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
             "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads",
             "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_rope_apply",
-            "gqa_attn_fwd_rope", "gqa_attn_bwd_rope")
+            "gqa_attn_fwd_rope", "gqa_attn_bwd_rope", "gqa_attn_fwd_fp8_workspace_bytes", "gqa_attn_fwd_fp8")
 
 
 class GqaError(RuntimeError):
@@ -48,6 +48,10 @@ class gqa_decode_problem(ctypes.Structure):
                 ("Sq", ctypes.c_int32), ("Skv", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class gqa_fp8_scales(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_float), ("k", ctypes.c_float), ("v", ctypes.c_float)]
 
 
 class gqa_rope(ctypes.Structure):
@@ -111,6 +115,10 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes.argtypes = [DP]
     lib.gqa_attn_decode.restype = ctypes.c_int
     lib.gqa_attn_decode.argtypes = [DP, vp, vp, vp, vp, fp, vp, ctypes.c_size_t, vp]
+    lib.gqa_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_attn_fwd_fp8_workspace_bytes.argtypes = [P]
+    lib.gqa_attn_fwd_fp8.restype = ctypes.c_int
+    lib.gqa_attn_fwd_fp8.argtypes = [P, ctypes.POINTER(gqa_fp8_scales), vp, vp, vp, vp, fp, vp, ctypes.c_size_t, vp]
     RP = ctypes.POINTER(gqa_rope)
     lib.gqa_rope_apply.restype = ctypes.c_int
     lib.gqa_rope_apply.argtypes = [RP, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -488,3 +496,42 @@ def gqa_attention_rope(q, k, v, causal=True, sliding_window=0, num_sinks=0, scal
     """(O, lse) with autograd, q and k rotated by YaRN RoPE (``rope``: a dict of gqa_rope
     fields or None for the model card's factor-32 setting)."""
     return GqaAttentionRope.apply(q, k, v, causal, sliding_window, num_sinks, scale, rope)
+
+
+# ---- FP8 forward ----
+def _fp8_problem(q8, k8, causal, window, num_sinks, scale):
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("q8 must be [B,H,S,D] and k8/v8 [B,G,S,D]")
+    B, H, S, D = q8.shape
+    if k8.shape[0] != B or k8.shape[2] != S or k8.shape[3] != D:
+        raise ValueError(f"k8 shape {tuple(k8.shape)} does not match q8 {tuple(q8.shape)}")
+    return make_problem(B, H, k8.shape[1], S, D, scale, causal, window, num_sinks, torch.bfloat16)
+
+
+def gqa_attn_fwd_fp8_workspace_bytes(q8, k8, causal=True, window=0, num_sinks=0, scale=None) -> int:
+    p = _fp8_problem(q8, k8, causal, window, num_sinks, scale)
+    return int(library().gqa_attn_fwd_fp8_workspace_bytes(ctypes.byref(p)))
+
+
+def gqa_attn_fwd_fp8(q8, k8, v8, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True, window=0, num_sinks=0,
+                     scale=None, out=None, lse=None, workspace=None, stream=None):
+    """(O bf16 [B,H,S,D], lse fp32 [B,H,S]) of attention over q_scale*q8, k_scale*k8,
+    v_scale*v8 (torch.float8_e4m3fn tensors)."""
+    e4m3 = torch.float8_e4m3fn
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _need(t, n, dtype=e4m3, device=q8.device)
+    _need(v8, "v8", shape=k8.shape)
+    p = _fp8_problem(q8, k8, causal, window, num_sinks, scale)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device) if lse is None else lse
+    _need(out, "out", dtype=torch.bfloat16, shape=q8.shape, device=q8.device)
+    _need(lse, "lse", dtype=torch.float32, shape=q8.shape[:3], device=q8.device)
+    nbytes = int(library().gqa_attn_fwd_fp8_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q8.device)
+    _need(workspace, "workspace", device=q8.device)
+    sc = gqa_fp8_scales(float(q_scale), float(k_scale), float(v_scale))
+    _check(library().gqa_attn_fwd_fp8(ctypes.byref(p), ctypes.byref(sc), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(out),
+                                      _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "gqa_attn_fwd_fp8")
+    return out, lse

@@ -521,6 +521,54 @@ int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot
   return hip_status(gqa::launch_rope(rk, GQA_F32, s));
 }
 
+size_t gqa_attn_fwd_fp8_workspace_bytes(const gqa_problem* p) {
+  if (check_problem(p) != GQA_OK || empty_problem(p) || p->S > (1 << 24)) return 0;
+  const size_t s_pad = ((size_t)p->S + gqa::kTile - 1) / gqa::kTile * gqa::kTile;
+  const size_t bytes = (size_t)p->B * p->G * gqa::kHeadDim * s_pad;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int gqa_attn_fwd_fp8(const gqa_problem* p, const gqa_fp8_scales* sc, const void* q8, const void* k8, const void* v8,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != GQA_OK) return rc;
+  if (sc == nullptr || !(isfinite(sc->q) && sc->q > 0.f) || !(isfinite(sc->k) && sc->k > 0.f) ||
+      !(isfinite(sc->v) && sc->v > 0.f))
+    return GQA_ERR_INVALID_ARG;
+  if (p->dtype != GQA_BF16 || p->S > (1 << 24)) return GQA_ERR_UNSUPPORTED;
+  if (empty_problem(p)) return GQA_OK;
+  if (!q8 || !k8 || !v8 || !o || !lse) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+    return GQA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < gqa_attn_fwd_fp8_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
+  gqa::Fp8FwdParams fp{};
+  fp.q = q8;
+  fp.k = k8;
+  fp.vt = workspace;
+  fp.o = o;
+  fp.lse = lse;
+  fp.B = p->B;
+  fp.H = p->H;
+  fp.G = p->G;
+  fp.S = p->S;
+  fp.s_pad = (p->S + gqa::kTile - 1) / gqa::kTile * gqa::kTile;
+  fp.scale_log2 = p->scale * sc->q * sc->k * kLog2e;
+  fp.o_scale = sc->v;
+  fp.mask = normalised_mask(p);
+  row_decomposition(p, &fp.hpw, &fp.qpw, &fp.n_qblk);
+  gqa::VtParams vp{};
+  vp.v = v8;
+  vp.vt = workspace;
+  vp.n_slabs = (long long)p->B * p->G;
+  vp.S = p->S;
+  vp.s_pad = fp.s_pad;
+  if (!grid_ok((long long)fp.n_qblk * p->B * (p->H / fp.hpw)) || !grid_ok(vp.n_slabs * (fp.s_pad / gqa::kTile)))
+    return GQA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = hip_status(gqa::launch_vt_permute(vp, s))) != GQA_OK) return rc;
+  return hip_status(gqa::launch_fwd_fp8(fp, s));
+}
+
 size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p) {
   if (check_decode(p) != GQA_OK || empty_decode(p)) return 0;
   gqa::DecodeParams dp;

@@ -219,6 +219,32 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
 
+// FP8 forward: Q, K (e4m3, [B][H|G][S][64]) and V^T permuted by vt_permute ([B][G][64][s_pad]).
+struct Fp8FwdParams {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* o;           // bf16 [B][H][S][64]
+  float* lse;
+  int B, H, G, S;
+  int s_pad;         // S rounded up to a multiple of 64
+  float scale_log2;  // softmax scale * q and k dequantisation factors * log2(e)
+  float o_scale;     // V's dequantisation factor
+  MaskSpec mask;
+  int hpw, qpw, n_qblk;
+};
+
+struct VtParams {
+  const void* v;     // e4m3 [n_slabs][S][64]
+  void* vt;          // e4m3 [n_slabs][64][s_pad]
+  long long n_slabs;
+  int S;
+  int s_pad;
+};
+
+hipError_t launch_vt_permute(const VtParams& p, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t s);
+
 hipError_t launch_rope(const RopeParams& p, int dtype, hipStream_t s);
 int rope_rows_per_block(int dtype);
 
