@@ -436,7 +436,8 @@ def main():
         sys.exit(2)
     if args.reduce_counters:
         special = args.workload.startswith("decode") or args.workload == "rope_k"
-        name = args.workload if special else workload(args.workload).name + ("_rope" if args.rope else "")
+        name = args.workload if special else (workload(args.workload).name + ("_rope" if args.rope else "")
+                                              + ("_fp8" if args.fp8 else ""))
         reduce_counters(*args.reduce_counters, name)
         return
     long_step = args.workload == "long"
