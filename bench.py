@@ -397,6 +397,7 @@ def run_fp8(args, w):
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock_mhz = gqa.gqa_clock_probe()
     ms_call = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     ms_step = wall * 1e3 / args.steps
     pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
@@ -419,6 +420,8 @@ def run_fp8(args, w):
                    "flop_per_step": flop, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / MFMA_FP8_PEAK_TFLOPS, 2),
         "pct_of_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "mfma_clock_mhz": round(clock_mhz, 1),
+        "pct_of_peak_at_measured_clock": round(100 * value / (MFMA_FP8_PEAK_TFLOPS * clock_mhz / 2400.0), 2),
         "kernels": {"fwd_fp8": {"ms": round(ms_call, 5), "tflops": round(ach, 1)}},
         "roofline": {"bound": "mfma", "kernel": "fwd_fp8 (V^T permute + forward, one call)", "achieved": round(ach, 2),
                      "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
@@ -554,6 +557,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    clock_mhz = gqa.gqa_clock_probe()  # right after the timed steps, the device still warm
+
     per_kernel_ms = {}
     for i, name in enumerate(kernels):
         per_kernel_ms[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
@@ -613,6 +618,8 @@ def main():
                    "flop_per_step": step_flop, "parallelism": "none (1 GPU)",
                    "rope": dict(gqa.YARN_ROPE) if args.rope else None},
         "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "mfma_clock_mhz": round(clock_mhz, 1),
+        "pct_of_peak_at_measured_clock": round(100 * value / (MFMA_BF16_PEAK_TFLOPS * clock_mhz / 2400.0), 2),
         "kernels": detail,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -95,6 +95,14 @@ const char* gqa_status_str(int status);
  * 10 * D * pairs * B * H flop (S, dP, dV, dK, dQ). */
 int64_t gqa_visible_pairs(const gqa_problem* p);
 
+/* Shader clock under matrix-core load (a measurement helper, not part of the attention):
+ * `blocks` workgroups of 4 waves run `iters` iterations of four independent bf16 MFMA
+ * chains each; out[2 b] receives workgroup b's shader-clock cycles and out[2 b + 1] the
+ * 100 MHz reference ticks over the same interval (clock in MHz = 100 * out[2b] / out[2b+1]).
+ * out: device memory, 2 * blocks uint64, 16-byte aligned.  1 <= blocks <= 65536,
+ * 1 <= iters <= 10^7; GQA_ERR_INVALID_ARG otherwise. */
+int gqa_clock_probe(unsigned long long* out, int32_t blocks, int32_t iters, void* stream);
+
 /* Forward.  Reads Q, K, V; writes O (dtype) and lse (fp32, natural log, of the scaled
  * scores).  lse is what the backward needs to recompute P.
  * o_lo (optional, NULL to skip; must be NULL for GQA_F32): same shape and dtype as O,

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -282,3 +282,13 @@ def test_fp8_forward_argument_checks():
     assert call(p=gqa.make_problem(1, 4, 2, 128, D=128)) == binding.GQA_ERR_UNSUPPORTED
     e = gqa.make_problem(0, 4, 2, 128)
     assert call(p=e, q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0) == binding.GQA_OK
+
+
+def test_clock_probe_argument_checks():
+    lib = gqa.library()
+    I = binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_clock_probe(None, 256, 100, None) == I
+    assert lib.gqa_clock_probe(FAKE + 8, 256, 100, None) == I
+    assert lib.gqa_clock_probe(FAKE, 0, 100, None) == I
+    assert lib.gqa_clock_probe(FAKE, 256, 0, None) == I
+    assert lib.gqa_clock_probe(FAKE, 256, 10 ** 8, None) == I

@@ -27,7 +27,8 @@ EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_preprocess",
             "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads",
             "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_rope_apply",
-            "gqa_attn_fwd_rope", "gqa_attn_bwd_rope", "gqa_attn_fwd_fp8_workspace_bytes", "gqa_attn_fwd_fp8")
+            "gqa_attn_fwd_rope", "gqa_attn_bwd_rope", "gqa_attn_fwd_fp8_workspace_bytes", "gqa_attn_fwd_fp8",
+            "gqa_clock_probe")
 
 
 class GqaError(RuntimeError):
@@ -119,6 +120,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_fwd_fp8_workspace_bytes.argtypes = [P]
     lib.gqa_attn_fwd_fp8.restype = ctypes.c_int
     lib.gqa_attn_fwd_fp8.argtypes = [P, ctypes.POINTER(gqa_fp8_scales), vp, vp, vp, vp, fp, vp, ctypes.c_size_t, vp]
+    lib.gqa_clock_probe.restype = ctypes.c_int
+    lib.gqa_clock_probe.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
     RP = ctypes.POINTER(gqa_rope)
     lib.gqa_rope_apply.restype = ctypes.c_int
     lib.gqa_rope_apply.argtypes = [RP, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -535,3 +538,15 @@ def gqa_attn_fwd_fp8(q8, k8, v8, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=T
                                       _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "gqa_attn_fwd_fp8")
     return out, lse
+
+
+def gqa_clock_probe(blocks=None, iters=20000, stream=None):
+    """Median shader clock (MHz) over `blocks` workgroups (default: one per compute unit)
+    keeping the matrix cores busy for `iters` iterations."""
+    if blocks is None:
+        blocks = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    _check(library().gqa_clock_probe(_ptr(out), int(blocks), int(iters), _stream(stream)), "gqa_clock_probe")
+    torch.cuda.synchronize()
+    c = out.view(blocks, 2).double().cpu()
+    return float((100.0 * c[:, 0] / c[:, 1]).median())

@@ -370,6 +370,12 @@ int64_t gqa_visible_pairs(const gqa_problem* p) {
 }
 
 
+int gqa_clock_probe(unsigned long long* out, int32_t blocks, int32_t iters, void* stream) {
+  if (out == nullptr || !aligned16(out) || blocks < 1 || blocks > 65536 || iters < 1 || iters > 10000000)
+    return GQA_ERR_INVALID_ARG;
+  return hip_status(gqa::launch_clock_probe(out, blocks, iters, (hipStream_t)stream));
+}
+
 int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, void* o, void* o_lo,
                  float* lse, void* stream) {
   int rc = check_problem(p);

@@ -242,6 +242,7 @@ struct VtParams {
   int s_pad;
 };
 
+hipError_t launch_clock_probe(unsigned long long* out, int blocks, int iters, hipStream_t s);
 hipError_t launch_vt_permute(const VtParams& p, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t s);
 
