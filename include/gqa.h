@@ -249,9 +249,11 @@ int gqa_attn_fwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q, co
                       void* o, void* o_lo, float* lse, void* q_rot, void* k_rot, void* stream);
 
 /* Backward of gqa_attn_fwd_rope: dQ, dK, dV of L = <O, dO> with respect to the unrotated
- * Q, K and V.  Takes the rotated q_rot and k_rot of the forward; runs gqa_attn_bwd on them
- * (which yields the gradients with respect to R Q and R K), then rotates dQ and dK back in
- * place with m R^T.  Workspace and errors as gqa_attn_bwd (gqa_attn_bwd_workspace_bytes). */
+ * Q, K and V.  Takes the rotated q_rot and k_rot of the forward; computes what gqa_attn_bwd
+ * gives for them (the gradients with respect to R Q and R K) and rotates dQ and dK back
+ * with m R^T: for 16-bit inputs inside the dK/dV and dQ kernels as they store their results
+ * (bit-identical to a separate rotation), for GQA_F32 by the rotation kernel in place
+ * afterwards.  Workspace and errors as gqa_attn_bwd (gqa_attn_bwd_workspace_bytes). */
 int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot, const void* k_rot,
                       const void* v, const void* o, const void* o_lo, const float* lse, const void* d_o,
                       float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
