@@ -21,8 +21,8 @@ What is compared, and the bounds:
     which on a row with few keys moves lse by up to that amount.
   * against the exact rotation (no rounding of q', k'): the mean abs errors of O, dQ, dK,
     dV within the same mean bounds, and lse per row within
-    1e-3 + scale * 2 * 2^-9 * max_j sum_c |q'_ic| |k'_jc| (the most that rounding q' and k'
-    to bf16 can move a score).
+    1e-3 + scale * 2 * 2^-8 * max_j sum_c |q'_ic| |k'_jc| (the most that rounding q' and k'
+    to bf16, 2^-8 relative each with its 8-bit significand, can move a score).
 Small cases are compared in full, the model card's long-context setting on sampled rows,
 keys and identities.
 """
@@ -219,7 +219,7 @@ def check_rope_full(w: Workload):
     _err("dK", got["dK"], dK2, GRAD_MAX, GRAD_MEAN)
     _err("dV", got["dV"], dV2, LP_MAX, LP_MEAN)
     # and against the exact rotation
-    bound = np.stack([np.stack([_lse_bound(QR[b, h], KR[b, h // hpg], pos, w, 2.0 ** -9) for h in range(w.H)])
+    bound = np.stack([np.stack([_lse_bound(QR[b, h], KR[b, h // hpg], pos, w, 2.0 ** -8) for h in range(w.H)])
                       for b in range(w.B)])
     _check_lse_exact(got["lse"], L, bound)
     for name, want, tol in (("O", O, LP_MEAN), ("dQ", dQ, GRAD_MEAN), ("dK", dK, GRAD_MEAN), ("dV", dV, LP_MEAN)):
