@@ -46,7 +46,10 @@
  *
  * Supported: D == 64; dtype GQA_BF16 and GQA_F16 (MFMA kernels) and GQA_F32 (fp32
  * kernels for reference-precision runs).  causal == 0 means full (non-causal)
- * attention and then requires window == 0 and num_sinks == 0.
+ * attention and then requires window == 0 and num_sinks == 0.  Sequences (S, and a
+ * decode cache's Skv) hold at most GQA_MAX_SEQ = 2^23 positions: the kernels address a
+ * head's rows with 32-bit byte offsets, tile padding included; longer ones return
+ * GQA_ERR_UNSUPPORTED.
  */
 #ifndef GQA_H_
 #define GQA_H_
@@ -59,6 +62,7 @@ extern "C" {
 #endif
 
 #define GQA_ABI_VERSION 1
+#define GQA_MAX_SEQ (1 << 23) /* longest S / Skv the attention entry points accept */
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -194,8 +198,8 @@ size_t gqa_attn_decode_workspace_bytes(const gqa_decode_problem* p);
  * memory, at least gqa_attn_decode_workspace_bytes, 16-byte aligned) is scratch owned by the
  * caller; its contents need no initialisation and are meaningless afterwards.  Errors:
  * GQA_ERR_INVALID_ARG for bad sizes, pointers or alignment (Sq > Skv included),
- * GQA_ERR_UNSUPPORTED for D != 64 or GQA_F32, GQA_ERR_WORKSPACE for a missing or short
- * workspace, GQA_ERR_HIP if a launch fails.  B == 0 returns GQA_OK without a launch. */
+ * GQA_ERR_UNSUPPORTED for D != 64, GQA_F32 or Skv > GQA_MAX_SEQ, GQA_ERR_WORKSPACE for a
+ * missing or short workspace, GQA_ERR_HIP if a launch fails.  B == 0 returns GQA_OK without a launch. */
 int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, const void* v,
                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -271,7 +275,7 @@ int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot
  * the key order the kernel's operands need; its contents need no initialisation.
  * Errors as gqa_attn_fwd, plus GQA_ERR_INVALID_ARG for a missing or non-positive scale,
  * GQA_ERR_WORKSPACE for a missing or short workspace, GQA_ERR_UNSUPPORTED for an output
- * dtype other than GQA_BF16 or S > 2^24. */
+ * dtype other than GQA_BF16. */
 typedef struct gqa_fp8_scales {
   float q, k, v; /* element value = scale * e4m3 code value; finite and > 0 */
 } gqa_fp8_scales;

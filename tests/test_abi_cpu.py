@@ -32,6 +32,17 @@ def test_library_exports_every_declared_symbol():
     assert gqa.abi_version() == 1
 
 
+def test_header_constants_match_the_binding():
+    text = open(os.path.join(ROOT, "include", "gqa.h")).read()
+    assert int(re.search(r"#define GQA_ABI_VERSION (\d+)", text).group(1)) == gqa.abi_version()
+    shift = int(re.search(r"#define GQA_MAX_SEQ \(1 << (\d+)\)", text).group(1))
+    assert binding.GQA_MAX_SEQ == 1 << shift
+    for name, value in re.findall(r"\b(GQA_(?:OK|ERR_\w+)) = (\d+)", text):
+        assert getattr(binding, name) == int(value), name
+    for name, value in re.findall(r"\b(GQA_(?:F32|BF16|F16)) = (\d+)", text):
+        assert getattr(binding, name) == int(value), name
+
+
 def test_status_strings():
     for s in range(5):
         assert gqa.status_str(s).startswith("GQA_")
@@ -62,6 +73,8 @@ def _fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, o_lo=None):
     (dict(dtype=7), binding.GQA_ERR_INVALID_ARG),
     (dict(D=128), binding.GQA_ERR_UNSUPPORTED),
     (dict(D=32), binding.GQA_ERR_UNSUPPORTED),
+    (dict(S=binding.GQA_MAX_SEQ + 1), binding.GQA_ERR_UNSUPPORTED),
+    (dict(S=binding.GQA_MAX_SEQ + 1, dtype=binding.GQA_F32), binding.GQA_ERR_UNSUPPORTED),
 ])
 def test_fwd_validation(kw, status):
     args = dict(B=1, H=4, G=2, S=128, D=64, scale=0.125, causal=1, window=0, num_sinks=0, dtype=binding.GQA_BF16)
@@ -110,6 +123,11 @@ def test_bwd_validation_and_workspace():
     assert lib.gqa_attn_bwd_grads(ctypes.byref(bad), *([FAKE] * 9), None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, None, None, FAKE, None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE + 2, FAKE, FAKE, None) == binding.GQA_ERR_INVALID_ARG
+    # sequences beyond the 32-bit in-slab addressing
+    long_p = gqa.make_problem(1, 2, 1, binding.GQA_MAX_SEQ + 1)
+    assert lib.gqa_attn_bwd_workspace_bytes(ctypes.byref(long_p)) == 0
+    assert lib.gqa_attn_bwd(ctypes.byref(long_p), *([FAKE] * 10), FAKE, 1 << 40, None) == binding.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_attn_bwd_grads(ctypes.byref(long_p), *([FAKE] * 9), None) == binding.GQA_ERR_UNSUPPORTED
 
 
 def _dec(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
@@ -130,7 +148,7 @@ def _dec(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40)
     (dict(dtype=7), binding.GQA_ERR_INVALID_ARG),
     (dict(dtype=binding.GQA_F32), binding.GQA_ERR_UNSUPPORTED),
     (dict(D=128), binding.GQA_ERR_UNSUPPORTED),
-    (dict(Skv=(1 << 24) + 1), binding.GQA_ERR_UNSUPPORTED),
+    (dict(Skv=binding.GQA_MAX_SEQ + 1), binding.GQA_ERR_UNSUPPORTED),
 ])
 def test_decode_validation(kw, status):
     args = dict(B=1, H=8, G=2, Sq=1, Skv=4096, D=64, scale=0.125, window=0, num_sinks=0, dtype=binding.GQA_BF16)
@@ -280,6 +298,8 @@ def test_fp8_forward_argument_checks():
     assert call(wsb=need - 1) == binding.GQA_ERR_WORKSPACE
     assert call(p=gqa.make_problem(1, 4, 2, 128, dtype=binding.GQA_F16)) == binding.GQA_ERR_UNSUPPORTED
     assert call(p=gqa.make_problem(1, 4, 2, 128, D=128)) == binding.GQA_ERR_UNSUPPORTED
+    assert call(p=gqa.make_problem(1, 4, 2, binding.GQA_MAX_SEQ + 1)) == binding.GQA_ERR_UNSUPPORTED
+    assert lib.gqa_attn_fwd_fp8_workspace_bytes(ctypes.byref(gqa.make_problem(1, 4, 2, binding.GQA_MAX_SEQ + 1))) == 0
     e = gqa.make_problem(0, 4, 2, 128)
     assert call(p=e, q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0) == binding.GQA_OK
 

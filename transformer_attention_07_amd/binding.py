@@ -21,6 +21,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so"
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
+GQA_MAX_SEQ = 1 << 23   # longest S / Skv the attention entry points accept
 _DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_F16}
 
 EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",

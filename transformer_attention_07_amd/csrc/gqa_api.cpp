@@ -4,6 +4,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <climits>
 
 #include "gqa_internal.h"
@@ -29,7 +30,7 @@ int check_problem(const gqa_problem* p) {
   if (p->causal == 0 && (p->window != 0 || p->num_sinks != 0)) return GQA_ERR_INVALID_ARG;
   if (p->dtype != GQA_F32 && p->dtype != GQA_BF16 && p->dtype != GQA_F16) return GQA_ERR_INVALID_ARG;
   if ((long long)p->B * p->H > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
-  if (p->D != gqa::kHeadDim) return GQA_ERR_UNSUPPORTED;
+  if (p->D != gqa::kHeadDim || p->S > GQA_MAX_SEQ) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
@@ -63,13 +64,16 @@ int grid_ok(long long blocks) { return blocks > 0 && blocks <= INT_MAX; }
 
 // Compute units of the current device (cached per device; 0 if the query fails).
 int current_cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};  // calls may come from several host threads
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -168,8 +172,7 @@ int check_decode(const gqa_decode_problem* p) {
   if (p->dtype != GQA_F32 && p->dtype != GQA_BF16 && p->dtype != GQA_F16) return GQA_ERR_INVALID_ARG;
   if (p->Sq > p->Skv) return GQA_ERR_INVALID_ARG;  // the rows are the newest Sq positions of the cache
   if (p->D != gqa::kHeadDim || p->dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
-  // in-slab byte offsets of the cache (Skv * 128) and the row count stay in 32 bits
-  if (p->Skv > (1 << 24) || (long long)p->B * p->H * p->Sq > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  if (p->Skv > GQA_MAX_SEQ || (long long)p->B * p->H * p->Sq > INT_MAX / 2) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
@@ -528,7 +531,7 @@ int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot
 }
 
 size_t gqa_attn_fwd_fp8_workspace_bytes(const gqa_problem* p) {
-  if (check_problem(p) != GQA_OK || empty_problem(p) || p->S > (1 << 24)) return 0;
+  if (check_problem(p) != GQA_OK || empty_problem(p)) return 0;
   const size_t s_pad = ((size_t)p->S + gqa::kTile - 1) / gqa::kTile * gqa::kTile;
   const size_t bytes = (size_t)p->B * p->G * gqa::kHeadDim * s_pad;
   return (bytes + 255) & ~(size_t)255;
@@ -541,7 +544,7 @@ int gqa_attn_fwd_fp8(const gqa_problem* p, const gqa_fp8_scales* sc, const void*
   if (sc == nullptr || !(isfinite(sc->q) && sc->q > 0.f) || !(isfinite(sc->k) && sc->k > 0.f) ||
       !(isfinite(sc->v) && sc->v > 0.f))
     return GQA_ERR_INVALID_ARG;
-  if (p->dtype != GQA_BF16 || p->S > (1 << 24)) return GQA_ERR_UNSUPPORTED;
+  if (p->dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   if (empty_problem(p)) return GQA_OK;
   if (!q8 || !k8 || !v8 || !o || !lse) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
