@@ -38,6 +38,9 @@
  * passed as void*; NULL = the null stream) and returns.  Results are ready when the
  * stream reaches that point.  The library keeps no state between calls, so calls on
  * different streams may run concurrently if their output buffers do not overlap.
+ * Within a call, an output (workspaces included) may overlap neither an input nor another
+ * output, except in gqa_rope_apply's in-place form; such a call returns
+ * GQA_ERR_INVALID_ARG before anything is enqueued.
  *
  * Errors.  Every argument is validated on the host before any HIP call; a non-OK
  * status means nothing was enqueued, except GQA_ERR_HIP (a launch failed: earlier

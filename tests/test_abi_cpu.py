@@ -312,3 +312,54 @@ def test_clock_probe_argument_checks():
     assert lib.gqa_clock_probe(FAKE, 0, 100, None) == I
     assert lib.gqa_clock_probe(FAKE, 256, 0, None) == I
     assert lib.gqa_clock_probe(FAKE, 256, 10 ** 8, None) == I
+
+
+def test_outputs_overlapping_inputs_or_outputs_are_rejected():
+    # distinct, far-apart fake device addresses, all 16-byte aligned: each call below differs
+    # from a valid one only in the overlap, and is refused before any HIP call
+    lib = gqa.library()
+    I = binding.GQA_ERR_INVALID_ARG
+    q, k, v, o, olo, lse, do, dq, dk, dv, ws, qr, kr = (FAKE + i * (1 << 32) for i in range(13))
+    p = gqa.make_problem(1, 4, 2, 128)     # Q/O bytes 65536, K/V 32768, lse 2048
+    P = ctypes.byref(p)
+    big = 1 << 40
+    # forward: O over K, lse inside Q, o_lo over O
+    assert lib.gqa_attn_fwd(P, q, k, v, k, None, lse, None) == I
+    assert lib.gqa_attn_fwd(P, q, k, v, o, None, q + 256, None) == I
+    assert lib.gqa_attn_fwd(P, q, k, v, o, o + 4096, lse, None) == I
+    # backward: dQ over Q, dK over dV, the delta workspace over lse
+    assert lib.gqa_attn_bwd(P, q, k, v, o, olo, lse, do, q, dk, dv, ws, big, None) == I
+    assert lib.gqa_attn_bwd(P, q, k, v, o, olo, lse, do, dq, dk, dk + 1024, ws, big, None) == I
+    assert lib.gqa_attn_bwd(P, q, k, v, o, olo, lse, do, dq, dk, dv, lse, big, None) == I
+    assert lib.gqa_attn_bwd_preprocess(P, o, olo, do, o + 512, None) == I
+    assert lib.gqa_attn_bwd_dkdv(P, q, k, v, lse, do, ws, k, dv, None) == I
+    assert lib.gqa_attn_bwd_dq(P, q, k, v, lse, do, ws, do, None) == I
+    assert lib.gqa_attn_bwd_grads(P, q, k, v, lse, do, ws, dq, dk, ws + 16, None) == I
+    # RoPE: the stored rotated Q over O, dV over V
+    r = ctypes.byref(binding.make_rope())
+    assert lib.gqa_attn_fwd_rope(P, r, q, k, v, o, None, lse, o + 64, kr, None) == I
+    assert lib.gqa_attn_bwd_rope(P, r, qr, kr, v, o, olo, lse, do, dq, dk, v, ws, big, None) == I
+    # FP8 (e4m3 Q8 is 32768 bytes): O inside Q8, the V^T workspace over V8
+    sc = ctypes.byref(binding.gqa_fp8_scales(1.0, 1.0, 1.0))
+    assert lib.gqa_attn_fwd_fp8(P, sc, q, k, v, q + 16384, lse, ws, big, None) == I
+    assert lib.gqa_attn_fwd_fp8(P, sc, q, k, v, o, lse, v, big, None) == I
+    # decode: O over K, the workspace over Q
+    d = binding.gqa_decode_problem(1, 8, 2, 1, 4096, 64, 0.125, 0, 0, binding.GQA_BF16)
+    D = ctypes.byref(d)
+    assert lib.gqa_attn_decode(D, q, k, v, k, lse, ws, big, None) == I
+    assert lib.gqa_attn_decode(D, q, k, v, o, lse, q, big, None) == I
+    # control: with no GPU present, the same calls with distinct buffers pass validation and
+    # fail only at the launch (never run where a device exists: the pointers are fake)
+    import torch
+    if torch.cuda.device_count() == 0:
+        H = binding.GQA_ERR_HIP
+        assert lib.gqa_attn_fwd(P, q, k, v, o, olo, lse, None) == H
+        assert lib.gqa_attn_bwd(P, q, k, v, o, olo, lse, do, dq, dk, dv, ws, big, None) == H
+        assert lib.gqa_attn_bwd_preprocess(P, o, olo, do, ws, None) == H
+        assert lib.gqa_attn_bwd_dkdv(P, q, k, v, lse, do, ws, dk, dv, None) == H
+        assert lib.gqa_attn_bwd_dq(P, q, k, v, lse, do, ws, dq, None) == H
+        assert lib.gqa_attn_bwd_grads(P, q, k, v, lse, do, ws, dq, dk, dv, None) == H
+        assert lib.gqa_attn_fwd_rope(P, r, q, k, v, o, None, lse, qr, kr, None) == H
+        assert lib.gqa_attn_bwd_rope(P, r, qr, kr, v, o, olo, lse, do, dq, dk, dv, ws, big, None) == H
+        assert lib.gqa_attn_fwd_fp8(P, sc, q, k, v, o, lse, ws, big, None) == H
+        assert lib.gqa_attn_decode(D, q, k, v, o, lse, ws, big, None) == H

@@ -161,10 +161,19 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int | None:
+def _stream(stream, device=None) -> int | None:
+    """The hipStream_t to enqueue on: the given stream, else the current stream of
+    ``device`` (the tensors' device)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     return getattr(stream, "cuda_stream", stream)
+
+
+def _run(device, what, fn, *args):
+    """Call library function ``fn`` with ``device`` as the current HIP device (the C-ABI
+    works on the current device's memory and sizes its launches for that device)."""
+    with torch.cuda.device(device):
+        _check(fn(*args), what)
 
 
 def _problem_from(q, k, causal, window, num_sinks, scale) -> gqa_problem:
@@ -220,8 +229,8 @@ def gqa_attn_fwd(q, k, v, causal=True, window=0, num_sinks=0, scale=None, out=No
         o_lo = torch.empty_like(q)
     if o_lo is not None:
         _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
-    _check(library().gqa_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(o_lo),
-                                  _ptr(lse), _stream(stream)), "gqa_attn_fwd")
+    _run(q.device, "gqa_attn_fwd", library().gqa_attn_fwd,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(o_lo), _ptr(lse), _stream(stream, q.device))
     return (out, lse, o_lo) if o_lo is not None else (out, lse)
 
 
@@ -263,9 +272,9 @@ def gqa_attn_bwd(q, k, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(library().gqa_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse),
-                                  _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
-                                  _stream(stream)), "gqa_attn_bwd")
+    _run(q.device, "gqa_attn_bwd", library().gqa_attn_bwd,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
+         _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream, q.device))
     return dq, dk, dv
 
 
@@ -280,8 +289,8 @@ def gqa_attn_bwd_preprocess(o, d_o, delta=None, stream=None, o_lo=None):
         delta = torch.empty((B, H, S), dtype=torch.float32, device=o.device)
     _need(delta, "delta", dtype=torch.float32, shape=(B, H, S), device=o.device)
     p = make_problem(B, H, 1, S, D, None, True, 0, 0, o.dtype)
-    _check(library().gqa_attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(o_lo), _ptr(d_o), _ptr(delta),
-                                             _stream(stream)), "gqa_attn_bwd_preprocess")
+    _run(o.device, "gqa_attn_bwd_preprocess", library().gqa_attn_bwd_preprocess,
+         ctypes.byref(p), _ptr(o), _ptr(o_lo), _ptr(d_o), _ptr(delta), _stream(stream, o.device))
     return delta
 
 
@@ -291,9 +300,9 @@ def gqa_attn_bwd_dkdv(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks
     _check_bwd_inputs(q, k, v, q, lse, d_o)
     _need(delta, "delta", dtype=torch.float32, shape=q.shape[:3], device=q.device)
     _, dk, dv = _grad_buffers(q, k, q.new_empty(q.shape, dtype=torch.float32), dk, dv)
-    _check(library().gqa_attn_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
-                                       _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)),
-           "gqa_attn_bwd_dkdv")
+    _run(q.device, "gqa_attn_bwd_dkdv", library().gqa_attn_bwd_dkdv,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dk), _ptr(dv),
+         _stream(stream, q.device))
     return dk, dv
 
 
@@ -305,8 +314,9 @@ def gqa_attn_bwd_dq(q, k, v, lse, d_o, delta, causal=True, window=0, num_sinks=0
     if dq is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _need(dq, "dq", dtype=torch.float32, shape=q.shape, device=q.device)
-    _check(library().gqa_attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
-                                     _ptr(delta), _ptr(dq), _stream(stream)), "gqa_attn_bwd_dq")
+    _run(q.device, "gqa_attn_bwd_dq", library().gqa_attn_bwd_dq,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dq),
+         _stream(stream, q.device))
     return dq
 
 
@@ -318,9 +328,9 @@ def gqa_attn_bwd_grads(q, k, v, lse, d_o, delta, causal=True, window=0, num_sink
     _check_bwd_inputs(q, k, v, q, lse, d_o)
     _need(delta, "delta", dtype=torch.float32, shape=q.shape[:3], device=q.device)
     dq, dk, dv = _grad_buffers(q, k, dq, dk, dv)
-    _check(library().gqa_attn_bwd_grads(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o),
-                                        _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
-           "gqa_attn_bwd_grads")
+    _run(q.device, "gqa_attn_bwd_grads", library().gqa_attn_bwd_grads,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+         _stream(stream, q.device))
     return dq, dk, dv
 
 
@@ -374,7 +384,8 @@ def _decode_problem_from(q, k, window, num_sinks, scale) -> gqa_decode_problem:
 
 def gqa_attn_decode_workspace_bytes(q, k, window=0, num_sinks=0, scale=None) -> int:
     p = _decode_problem_from(q, k, window, num_sinks, scale)
-    return int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
+    with torch.cuda.device(q.device):   # sized for the device's compute units
+        return int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
 
 
 def gqa_attn_decode(q, k, v, window=0, num_sinks=0, scale=None, out=None, lse=None, workspace=None,
@@ -391,13 +402,15 @@ def gqa_attn_decode(q, k, v, window=0, num_sinks=0, scale=None, out=None, lse=No
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _need(out, "out", dtype=q.dtype, shape=q.shape, device=q.device)
     _need(lse, "lse", dtype=torch.float32, shape=q.shape[:3], device=q.device)
-    nbytes = int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
+    with torch.cuda.device(q.device):
+        nbytes = int(library().gqa_attn_decode_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(library().gqa_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                     _ptr(workspace), ws_bytes, _stream(stream)), "gqa_attn_decode")
+    _run(q.device, "gqa_attn_decode", library().gqa_attn_decode,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+         _stream(stream, q.device))
     return out, lse
 
 
@@ -416,8 +429,9 @@ def gqa_rope_apply(x, pos0=0, inverse=False, rope=None, out=None, stream=None):
     S, D = x.shape[-2], x.shape[-1]
     n = x.numel() // (S * D) if S * D else 0
     r = _rope_arg(rope)
-    _check(library().gqa_rope_apply(ctypes.byref(r), _ptr(x), _ptr(out), n, S, D, int(pos0), int(bool(inverse)),
-                                    _DTYPES[x.dtype], _stream(stream)), "gqa_rope_apply")
+    _run(x.device, "gqa_rope_apply", library().gqa_rope_apply,
+         ctypes.byref(r), _ptr(x), _ptr(out), n, S, D, int(pos0), int(bool(inverse)), _DTYPES[x.dtype],
+         _stream(stream, x.device))
     return out
 
 
@@ -445,9 +459,9 @@ def gqa_attn_fwd_rope(q, k, v, causal=True, window=0, num_sinks=0, scale=None, r
     if o_lo is not None:
         _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
     r = _rope_arg(rope)
-    _check(library().gqa_attn_fwd_rope(ctypes.byref(p), ctypes.byref(r), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                       _ptr(o_lo), _ptr(lse), _ptr(q_rot), _ptr(k_rot), _stream(stream)),
-           "gqa_attn_fwd_rope")
+    _run(q.device, "gqa_attn_fwd_rope", library().gqa_attn_fwd_rope,
+         ctypes.byref(p), ctypes.byref(r), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(o_lo), _ptr(lse), _ptr(q_rot),
+         _ptr(k_rot), _stream(stream, q.device))
     res = (out, lse, q_rot, k_rot)
     return res + (o_lo,) if o_lo is not None else res
 
@@ -467,9 +481,9 @@ def gqa_attn_bwd_rope(q_rot, k_rot, v, o, lse, d_o, causal=True, window=0, num_s
     _need(workspace, "workspace", device=q_rot.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     r = _rope_arg(rope)
-    _check(library().gqa_attn_bwd_rope(ctypes.byref(p), ctypes.byref(r), _ptr(q_rot), _ptr(k_rot), _ptr(v),
-                                       _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
-                                       _ptr(workspace), ws_bytes, _stream(stream)), "gqa_attn_bwd_rope")
+    _run(q_rot.device, "gqa_attn_bwd_rope", library().gqa_attn_bwd_rope,
+         ctypes.byref(p), ctypes.byref(r), _ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse),
+         _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream, q_rot.device))
     return dq, dk, dv
 
 
@@ -535,9 +549,9 @@ def gqa_attn_fwd_fp8(q8, k8, v8, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=T
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q8.device)
     _need(workspace, "workspace", device=q8.device)
     sc = gqa_fp8_scales(float(q_scale), float(k_scale), float(v_scale))
-    _check(library().gqa_attn_fwd_fp8(ctypes.byref(p), ctypes.byref(sc), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(out),
-                                      _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream(stream)), "gqa_attn_fwd_fp8")
+    _run(q8.device, "gqa_attn_fwd_fp8", library().gqa_attn_fwd_fp8,
+         ctypes.byref(p), ctypes.byref(sc), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), _ptr(workspace),
+         workspace.numel() * workspace.element_size(), _stream(stream, q8.device))
     return out, lse
 
 

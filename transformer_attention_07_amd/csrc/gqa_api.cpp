@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <climits>
+#include <initializer_list>
 
 #include "gqa_internal.h"
 
@@ -106,6 +107,35 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 }
 
 size_t elem_bytes(int dtype) { return dtype == GQA_F32 ? 4 : 2; }
+
+// A buffer the call reads or writes: address and bytes (nullptr: absent).
+struct Span {
+  const void* ptr;
+  size_t bytes;
+};
+
+// True if an output overlaps an input or another output.  Every kernel reads its inputs
+// while other workgroups write outputs, so no aliasing is allowed except where an entry
+// point says so (the rotation's in-place form).
+bool aliased(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Span& i : ins)
+      if (overlaps(o->ptr, o->bytes, i.ptr, i.bytes)) return true;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlaps(o->ptr, o->bytes, o2->ptr, o2->bytes)) return true;
+  }
+  return false;
+}
+
+// Byte sizes of a problem's tensors (see the layout in gqa.h).
+struct Sizes {
+  size_t q, kv, row, q32, kv32;  // Q/O/dO, K/V (element type); lse/delta; dQ; dK/dV
+};
+Sizes sizes_of(const gqa_problem* p) {
+  const size_t rows_q = (size_t)p->B * p->H * p->S, rows_kv = (size_t)p->B * p->G * p->S;
+  const size_t e = elem_bytes(p->dtype), D = (size_t)p->D;
+  return Sizes{rows_q * D * e, rows_kv * D * e, rows_q * sizeof(float), rows_q * D * 4, rows_kv * D * 4};
+}
 
 // The configuration as the kernels take it: YaRN's per-pair frequencies (RoFormer's
 // base^(-2i/D), kept for pairs that turn more than beta times over the original context,
@@ -267,6 +297,8 @@ int run_dkdv(const gqa_problem* p, const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
       !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
     return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{dk, z.kv32}, {dv, z.kv32}}, {{q, z.q}, {k, z.kv}, {v, z.kv}, {lse, z.row}, {d_o, z.q}, {delta, z.row}})) return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   bp.q = q;
@@ -291,6 +323,8 @@ int run_dq(const gqa_problem* p, const void* q, const void* k, const void* v, co
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
       !aligned16(delta) || !aligned16(dq))
     return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{dq, z.q32}}, {{q, z.q}, {k, z.kv}, {v, z.kv}, {lse, z.row}, {d_o, z.q}, {delta, z.row}})) return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   bp.q = q;
@@ -314,6 +348,8 @@ int run_grads(const gqa_problem* p, const void* q, const void* k, const void* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(d_o) ||
       !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{dq, z.q32}, {dk, z.kv32}, {dv, z.kv32}}, {{q, z.q}, {k, z.kv}, {v, z.kv}, {lse, z.row}, {d_o, z.q}, {delta, z.row}})) return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   // When all dK/dV workgroups fit in one round of workgroup slots (two per CU), the causal
@@ -388,6 +424,8 @@ int gqa_attn_fwd(const gqa_problem* p, const void* q, const void* k, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_lo))
     return GQA_ERR_INVALID_ARG;
   if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{o, z.q}, {o_lo, z.q}, {lse, z.row}}, {{q, z.q}, {k, z.kv}, {v, z.kv}})) return GQA_ERR_INVALID_ARG;
   if (!fwd_grid_ok(p)) return GQA_ERR_UNSUPPORTED;
   return run_fwd(p, q, k, v, o, o_lo, lse, nullptr, nullptr, (hipStream_t)stream);
 }
@@ -422,11 +460,8 @@ int gqa_attn_fwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q, co
       !aligned16(q_rot) || !aligned16(k_rot))
     return GQA_ERR_INVALID_ARG;
   if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
-  const size_t row = (size_t)p->D * elem_bytes(p->dtype);
-  const size_t qb = (size_t)p->B * p->H * p->S * row, kb = (size_t)p->B * p->G * p->S * row;
-  if (overlaps(k_rot, kb, q, qb) || overlaps(k_rot, kb, k, kb) || overlaps(k_rot, kb, v, kb) ||
-      overlaps(q_rot, qb, q, qb) || overlaps(q_rot, qb, k, kb) || overlaps(q_rot, qb, v, kb) ||
-      overlaps(q_rot, qb, k_rot, kb))
+  const Sizes z = sizes_of(p);
+  if (aliased({{o, z.q}, {o_lo, z.q}, {lse, z.row}, {q_rot, z.q}, {k_rot, z.kv}}, {{q, z.q}, {k, z.kv}, {v, z.kv}}))
     return GQA_ERR_INVALID_ARG;
   if (!fwd_grid_ok(p)) return GQA_ERR_UNSUPPORTED;
   gqa::RopeParams rp;
@@ -450,6 +485,8 @@ int gqa_attn_bwd_preprocess(const gqa_problem* p, const void* o, const void* o_l
   if (!o || !d_o || !delta) return GQA_ERR_INVALID_ARG;
   if (!aligned16(o) || !aligned16(o_lo) || !aligned16(d_o) || !aligned16(delta)) return GQA_ERR_INVALID_ARG;
   if (o_lo != nullptr && p->dtype == GQA_F32) return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{delta, z.row}}, {{o, z.q}, {o_lo, z.q}, {d_o, z.q}})) return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   bp.o = o;
@@ -489,6 +526,10 @@ int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void*
     return GQA_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(p);
+  if (aliased({{dq, z.q32}, {dk, z.kv32}, {dv, z.kv32}, {workspace, z.row}},
+              {{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {o_lo, z.q}, {lse, z.row}, {d_o, z.q}}))
+    return GQA_ERR_INVALID_ARG;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   float* delta = (float*)workspace;
@@ -512,6 +553,10 @@ int gqa_attn_bwd_rope(const gqa_problem* p, const gqa_rope* r, const void* q_rot
       return GQA_ERR_INVALID_ARG;
     if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+    const Sizes z = sizes_of(p);
+    if (aliased({{dq, z.q32}, {dk, z.kv32}, {dv, z.kv32}, {workspace, z.row}},
+                {{q_rot, z.q}, {k_rot, z.kv}, {v, z.kv}, {o, z.q}, {o_lo, z.q}, {lse, z.row}, {d_o, z.q}}))
+      return GQA_ERR_INVALID_ARG;
     BwdParams bp;
     if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
     float* delta = (float*)workspace;
@@ -550,6 +595,10 @@ int gqa_attn_fwd_fp8(const gqa_problem* p, const gqa_fp8_scales* sc, const void*
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
     return GQA_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < gqa_attn_fwd_fp8_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
+  const Sizes z = sizes_of(p);  // element type bf16: the e4m3 inputs are half of those sizes
+  if (aliased({{o, z.q}, {lse, z.row}, {workspace, gqa_attn_fwd_fp8_workspace_bytes(p)}},
+              {{q8, z.q / 2}, {k8, z.kv / 2}, {v8, z.kv / 2}}))
+    return GQA_ERR_INVALID_ARG;
   gqa::Fp8FwdParams fp{};
   fp.q = q8;
   fp.k = k8;
@@ -598,6 +647,11 @@ int gqa_attn_decode(const gqa_decode_problem* p, const void* q, const void* k, c
   size_t need = 0;
   if ((rc = plan_decode(p, &dp, &need)) != GQA_OK) return rc;
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  const size_t e = elem_bytes(p->dtype), qrows = (size_t)p->B * p->H * p->Sq;
+  const size_t kvb = (size_t)p->B * p->G * p->Skv * p->D * e;
+  if (aliased({{o, qrows * p->D * e}, {lse, qrows * sizeof(float)}, {workspace, need}},
+              {{q, qrows * p->D * e}, {k, kvb}, {v, kvb}}))
+    return GQA_ERR_INVALID_ARG;
   dp.q = q;
   dp.k = k;
   dp.v = v;
