@@ -1,14 +1,16 @@
 """Property tests (hypothesis, derandomised): random small shapes -- S not a multiple of the
 64-row tile, windows shorter than a tile, sink counts off tile edges, every head grouping --
-through the C-ABI against the CPU fp64 oracle, for the forward + backward (bf16 and fp32),
-decode, the RoPE path and the FP8 forward.
+through the C-ABI against the CPU fp64 oracle, for the forward + backward (bf16, f16 and
+fp32), decode (bf16 and f16), the RoPE path and the FP8 forward.
 
-Bounds.  fp32: 1e-4 max abs on everything.  bf16: each element within the larger of the
-stated 2e-2 and the most the kernels' own bf16 roundings can move it, the mean within the
+Bounds.  fp32: 1e-4 max abs on everything.  16-bit: each element within the larger of the
+stated 2e-2 and the most the kernels' own roundings can move it, the mean within the
 larger of 2e-3 and twice the expected size of those roundings (lse: 1e-3).  The kernels
-round to bf16 exactly the factors they hand to the matrix cores: P before P V (forward)
-and P^T dO (dV), dS before dS K (dQ) and dS^T Q (dK), and O on output; bf16 keeps an 8-bit
-significand, so each rounding moves a value x by at most 2^-8 |x|.  A product's error is
+round to the element type exactly the factors they hand to the matrix cores: P before P V
+(forward) and P^T dO (dV), dS before dS K (dQ) and dS^T Q (dK), and O on output; each
+rounding moves a value x by at most u |x|, u = 2^-8 for bf16 (8-bit significand) and
+2^-11 for f16 (11-bit; its subnormals below 2^-14 add at most 2^-25 absolute per term,
+inside the 1e-4 allowed for fp32 arithmetic at these sizes).  A product's error is
 then at most sum 2^-8 |x| |y| over its terms; for the mean each term's error is taken as
 uniform within that bound (variance (2^-8 x y)^2 / 3).  On the shapes of the named
 workloads the stated tolerances are the larger; on small shapes where a few large
@@ -62,14 +64,15 @@ def _err(got, want):
 
 
 U16 = 2.0 ** -8                    # bf16 unit roundoff
+UNIT_ROUNDOFF = {"bf16": U16, "f16": 2.0 ** -11}
 LP_MAX, LP_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
 TWICE_MEAN = 2.0 * np.sqrt(2.0 / np.pi)   # twice E|N(0, 1)|
 
 
-def _rounding_bounds(q, k, v, do, O, scale, causal, W, NS):
+def _rounding_bounds(q, k, v, do, O, scale, causal, W, NS, u=U16):
     """Per-element bounds and mean bounds {name: (tol, mean_tol)} for O, dQ, dK, dV from the
-    bf16 roundings of P, dS and O (see the module docstring); fp64 arrays of the values
-    the kernels multiply, q, do, O [B,H,S,D] and k, v [B,G,S,D]."""
+    roundings of P, dS and O to a type of unit roundoff ``u`` (see the module docstring);
+    fp64 arrays of the values the kernels multiply, q, do, O [B,H,S,D] and k, v [B,G,S,D]."""
     B, H, S, D = q.shape
     hpg = H // k.shape[1]
     rows = np.arange(S)
@@ -80,14 +83,14 @@ def _rounding_bounds(q, k, v, do, O, scale, causal, W, NS):
             g = h // hpg
             p, _ = ref._softmax_rows(ref._scores(q[b, h], k[b, g], rows, scale, causal, W, NS))
             ds = p * (do[b, h] @ v[b, g].T - (do[b, h] * O[b, h]).sum(axis=1, keepdims=True))
-            up, uds = U16 * p, U16 * scale * np.abs(ds)
+            up, uds = u * p, u * scale * np.abs(ds)
             for name, a, x, out in (("O", up, v[b, g], (b, h)), ("dV", up.T, do[b, h], (b, g)),
                                     ("dQ", uds, k[b, g], (b, h)), ("dK", uds.T, q[b, h], (b, g))):
                 tol[name][out] += a @ np.abs(x)
                 var[name][out] += (a ** 2) @ (x ** 2) / 3.0
     res = {n: [tol[n] + 1e-4, TWICE_MEAN * np.sqrt(var[n])] for n in tol}
-    res["O"][0] += U16 * np.abs(O)
-    res["O"][1] += U16 / 2.0 * np.abs(O)
+    res["O"][0] += u * np.abs(O)
+    res["O"][1] += u / 2.0 * np.abs(O)
     return res
 
 
@@ -114,11 +117,12 @@ def _np(t):
     return t.detach().double().cpu().numpy()
 
 
-@settings(max_examples=40, **SETTINGS)
-@given(shp=shapes(), f32=st.booleans(), seed=st.integers(0, 10 ** 6))
-def test_fwd_bwd_random_shapes(shp, f32, seed):
+@settings(max_examples=48, **SETTINGS)
+@given(shp=shapes(), dt=st.sampled_from(["bf16", "f32", "bf16", "f16"]), seed=st.integers(0, 10 ** 6))
+def test_fwd_bwd_random_shapes(shp, dt, seed):
     B, H, G, S, causal, W, NS = shp
-    w = Workload("prop", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, dtype="f32" if f32 else "bf16",
+    f32 = dt == "f32"
+    w = Workload("prop", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, dtype=dt,
                  direction="fwd+bwd", seed=seed)
     print(f"[prop] {w}", flush=True)
     q, k, v, do = make_inputs(w)
@@ -137,7 +141,7 @@ def test_fwd_bwd_random_shapes(shp, f32, seed):
         assert _err(_np(lse), L)[0] <= 1e-4
         return
     f64 = [ref._f64(x) for x in (q, k, v, do)]
-    bounds = _rounding_bounds(*f64, O, w.scale, causal, W, NS)
+    bounds = _rounding_bounds(*f64, O, w.scale, causal, W, NS, UNIT_ROUNDOFF[dt])
     for name in got:
         _check(name, _np(got[name]), want[name], bounds[name], LP_MAX, LP_MEAN)
     assert _err(_np(lse), L)[0] <= LSE_MAX
@@ -145,11 +149,12 @@ def test_fwd_bwd_random_shapes(shp, f32, seed):
 
 @settings(max_examples=16, **SETTINGS)
 @given(G=st.sampled_from([1, 2, 4]), hpg=st.sampled_from([1, 2, 4, 8, 16]), Skv=st.integers(1, 3000),
-       sq_frac=st.floats(0.0, 1.0), win=st.integers(0, 3000), ns=st.integers(0, 200), seed=st.integers(0, 10 ** 6))
-def test_decode_random_shapes(G, hpg, Skv, sq_frac, win, ns, seed):
+       sq_frac=st.floats(0.0, 1.0), win=st.integers(0, 3000), ns=st.integers(0, 200),
+       dt=st.sampled_from(["bf16", "bf16", "f16"]), seed=st.integers(0, 10 ** 6))
+def test_decode_random_shapes(G, hpg, Skv, sq_frac, win, ns, dt, seed):
     Sq = max(1, min(Skv, int(round(sq_frac * 20))))
     w = DecodeWorkload("prop_dec", B=1, H=G * hpg, G=G, Sq=Sq, Skv=Skv, window=win, num_sinks=ns if win else 0,
-                       seed=seed)
+                       dtype=dt, seed=seed)
     print(f"[prop] {w}", flush=True)
     q, k, v = make_decode_inputs(w)
     o, lse = gqa.gqa_attn_decode(q.cuda(), k.cuda(), v.cuda(), window=w.window, num_sinks=w.num_sinks)
