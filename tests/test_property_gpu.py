@@ -44,7 +44,7 @@ def shapes(draw, max_s=300):
     """(B, H, G, S, causal, W, NS): masks weighted towards windows, half of them shorter than
     one 64-row tile, with sink counts that mostly end inside a tile."""
     G = draw(st.sampled_from([1, 2, 4]))
-    hpg = draw(st.sampled_from([1, 2, 3, 4, 8]))
+    hpg = draw(st.sampled_from([1, 2, 3, 4, 6, 8, 16]))
     S = draw(st.integers(1, max_s))
     kind = draw(st.sampled_from(["causal", "full", "short_window", "window", "short_window", "window"]))
     causal, W, NS = kind != "full", 0, 0
@@ -148,7 +148,7 @@ def test_fwd_bwd_random_shapes(shp, dt, seed):
 
 
 @settings(max_examples=16, **SETTINGS)
-@given(G=st.sampled_from([1, 2, 4]), hpg=st.sampled_from([1, 2, 4, 8, 16]), Skv=st.integers(1, 3000),
+@given(G=st.sampled_from([1, 2, 4]), hpg=st.sampled_from([1, 2, 3, 4, 8, 16, 32]), Skv=st.integers(1, 3000),
        sq_frac=st.floats(0.0, 1.0), win=st.integers(0, 3000), ns=st.integers(0, 200),
        dt=st.sampled_from(["bf16", "bf16", "f16"]), seed=st.integers(0, 10 ** 6))
 def test_decode_random_shapes(G, hpg, Skv, sq_frac, win, ns, dt, seed):
