@@ -88,7 +88,7 @@ def source_digest():
 def load_traffic(kernel, wname):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it was
     taken on the current kernel sources; None otherwise."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -107,12 +107,16 @@ KERNEL_KEYS = {"rope_kernel": "rope", "fwd_fp8_kernel": "fwd_fp8", "vt_permute_k
 COPY_BYTES = 1 << 30
 
 
-def reduce_counters(fetch_csv, write_csv, wname):
+def reduce_counters(fetch_csv, write_csv, wname, path=None):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
-    scaled so that the 1 GiB calibration copy reads as exactly 1 GiB in and 1 GiB out."""
+    scaled so that the 1 GiB calibration copy reads as exactly 1 GiB in and 1 GiB out;
+    recorded under ``wname`` in ``path`` (default profiles/traffic.json)."""
     import csv
 
     def per_kernel(path, counter):
+        # a kernel's launches are alike: their mean.  The calibration copy is the largest
+        # copy dispatch: the runtime's copy kernel also serves small copies (reading a
+        # result back to the host), which must not dilute it.
         acc = {}
         with open(path) as f:
             for r in csv.DictReader(f):
@@ -121,11 +125,11 @@ def reduce_counters(fetch_csv, write_csv, wname):
                 key = next((v for k, v in KERNEL_KEYS.items() if k in r["Kernel_Name"]), None)
                 if key:
                     acc.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
-        return {k: sum(v) / len(v) for k, v in acc.items()}
+        return {k: max(v) if k == "copy" else sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_scale, w_scale = COPY_BYTES / fetch["copy"], COPY_BYTES / write["copy"]
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
