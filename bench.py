@@ -85,9 +85,9 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, wname):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
-    taken on the current kernel sources; None otherwise."""
+def load_traffic(kernel, wname, path=None):
+    """HBM bytes per launch of `kernel` from the committed counter summary (or `path`), if
+    it was taken on the current kernel sources; None otherwise."""
     path = path or os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:

@@ -8,6 +8,8 @@ import json
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
@@ -44,3 +46,18 @@ def test_counter_reduction_calibrates_on_the_large_copy(tmp_path):
     assert ent["fetch_bytes"] == 100 << 20 and ent["write_bytes"] == 40 << 20
     assert ent["bytes_per_launch"] == 140 << 20
     assert rec["source_digest"] == bench.source_digest()
+    # what the bench line's roofline reads back
+    assert bench.load_traffic("fwd", "wl", path=str(out)) == 140 << 20
+    assert bench.load_traffic("fwd", "other", path=str(out)) is None
+
+
+def test_committed_traffic_reads_back():
+    # every bench line reads the committed summary: it must parse and hold the default
+    # step's dominant kernel.  After a kernel change its digest is stale until counters are
+    # taken again on a GPU, and the bench then reports traffic as null.
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    assert "bwd_grads@step" in rec["kernels"] and rec["calibration"]
+    if rec["source_digest"] != bench.source_digest():
+        pytest.skip("counters predate the current kernel sources")
+    assert bench.load_traffic("bwd_grads", "step") == rec["kernels"]["bwd_grads@step"]["bytes_per_launch"]
