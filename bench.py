@@ -153,6 +153,20 @@ def reduce_counters(fetch_csv, write_csv, wname, path=None):
     print(json.dumps(rec["kernels"], indent=1))
 
 
+def host_cpu():
+    """The host CPU's model name (for the CPU baseline's record)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown CPU"
+
+
 def cpu_baseline(w, inputs, budget_s, rope=False):
     """The oracle, as it stands, on whole kv groups of the same workload until the
     time budget is used: forward rows of every head of the group plus its backward.
@@ -183,7 +197,7 @@ def cpu_baseline(w, inputs, budget_s, rope=False):
         dt = time.perf_counter() - t0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"{nrows} forward rows (chunks of 256 at seeded positions), {dt:.1f} s, fp64 numpy"}
+                "sample": f"{nrows} forward rows (chunks of 256 at seeded positions), {dt:.1f} s, fp64 numpy on {host_cpu()}"}
     hpg = w.H // w.G
     pairs = gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
     kw = dict(scale=w.scale, causal=w.causal, window=w.window, num_sinks=w.num_sinks)
@@ -209,7 +223,7 @@ def cpu_baseline(w, inputs, budget_s, rope=False):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{groups} of {w.B * w.G} kv groups (all {hpg} heads each, "
-                      f"{'fwd+bwd' if 'bwd' in w.direction else 'fwd'}), {dt:.1f} s, fp64 numpy"}
+                      f"{'fwd+bwd' if 'bwd' in w.direction else 'fwd'}), {dt:.1f} s, fp64 numpy on {host_cpu()}"}
 
 
 def decode_bytes(w):
@@ -282,7 +296,7 @@ def run_decode(args, w):
         dt = time.perf_counter() - t1
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         cpu = {"value": nbytes / w.B / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-               "sample": f"batch element 0 of {w.B} (all {w.H} heads, {w.Sq} rows each), {dt:.1f} s, fp64 numpy"}
+               "sample": f"batch element 0 of {w.B} (all {w.H} heads, {w.Sq} rows each), {dt:.1f} s, fp64 numpy on {host_cpu()}"}
     wl = (f"decode, B={w.B} H={w.H} G={w.G} Sq={w.Sq} Skv={w.Skv} d={w.D}"
           + (f" window={w.window} sinks={w.num_sinks}" if w.window else "") + f", {w.dtype}")
     line = {
@@ -347,7 +361,7 @@ def run_rope_k(args):
         dt = time.perf_counter() - t1
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         cpu = {"value": 2.0 * xs.numel() * 2 / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-               "sample": f"one [{S}][{D}] slab of {B * G}, {dt:.1f} s, fp64 numpy"}
+               "sample": f"one [{S}][{D}] slab of {B * G}, {dt:.1f} s, fp64 numpy on {host_cpu()}"}
     line = {
         "metric": "YaRN rotary embedding HBM throughput (algorithmic bytes / time)", "value": round(value, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
