@@ -1,7 +1,7 @@
 """Property tests (hypothesis, derandomised): random small shapes -- S not a multiple of the
 64-row tile, windows shorter than a tile, sink counts off tile edges, every head grouping --
 through the C-ABI against the CPU fp64 oracle, for the forward + backward (bf16, f16 and
-fp32), decode (bf16 and f16), the RoPE path and the FP8 forward.
+fp32), decode (bf16 and f16), the RoPE path (bf16, f16 and fp32) and the FP8 forward.
 
 Bounds.  fp32: 1e-4 max abs on everything.  16-bit: each element within the larger of the
 stated 2e-2 and the most the kernels' own roundings can move it, the mean within the
@@ -166,28 +166,39 @@ def test_decode_random_shapes(G, hpg, Skv, sq, win, ns, dt, seed):
     assert _err(_np(lse), L)[0] <= LSE_MAX
 
 
-@settings(max_examples=16, **SETTINGS)
-@given(shp=shapes(max_s=200), seed=st.integers(0, 10 ** 6))
-def test_rope_random_shapes(shp, seed):
+@settings(max_examples=24, **SETTINGS)
+@given(shp=shapes(max_s=200), dt=st.sampled_from(["bf16", "f16", "f32"]),
+       seed=st.integers(0, 10 ** 6))
+def test_rope_random_shapes(shp, dt, seed):
     B, H, G, S, causal, W, NS = shp
-    w = Workload("prop_rope", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, direction="fwd+bwd",
-                 seed=seed)
+    w = Workload("prop_rope", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, dtype=dt,
+                 direction="fwd+bwd", seed=seed)
     print(f"[prop] {w}", flush=True)
     q, k, v, do = make_inputs(w)
     kw = dict(causal=causal, window=W, num_sinks=NS)
-    o, lse, q_rot, k_rot, o_lo = gqa.gqa_attn_fwd_rope(q.cuda(), k.cuda(), v.cuda(), keep_residual=True, **kw)
+    res = gqa.gqa_attn_fwd_rope(q.cuda(), k.cuda(), v.cuda(), keep_residual=dt != "f32", **kw)
+    o, lse, q_rot, k_rot = res[:4]
+    o_lo = res[4] if len(res) > 4 else None
     dq, dk, dv = gqa.gqa_attn_bwd_rope(q_rot, k_rot, v.cuda(), o, lse, do.cuda(), o_lo=o_lo, **kw)
     torch.cuda.synchronize()
-    bf = torch.bfloat16
-    O, L = rref.forward(q, k, v, operand_dtype=bf, **kw)
-    dQ, dK, dV = rref.backward(q, k, v, do, operand_dtype=bf, **kw)
+    if dt == "f32":  # against the exact rotation
+        O, L = rref.forward(q, k, v, **kw)
+        dQ, dK, dV = rref.backward(q, k, v, do, **kw)
+        for name, got, want in (("O", o, O), ("lse", lse, L), ("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+            assert _err(_np(got), want)[0] <= 1e-4, name
+        return
+    td = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    O, L = rref.forward(q, k, v, operand_dtype=td, **kw)
+    dQ, dK, dV = rref.backward(q, k, v, do, operand_dtype=td, **kw)
     m = rref.yarn_mscale()
-    qs, ks = rref._rot_qk(q, k, rref.YARN, bf)          # the stored rotated operands
-    bounds = _rounding_bounds(qs, ks, ref._f64(v), ref._f64(do), O, w.scale, causal, W, NS)
+    qs, ks = rref._rot_qk(q, k, rref.YARN, td)          # the stored rotated operands
+    bounds = _rounding_bounds(qs, ks, ref._f64(v), ref._f64(do), O, w.scale, causal, W, NS, UNIT_ROUNDOFF[dt])
     for name, got, want, lp in (("O", o, O, 1.0), ("dQ", dq, dQ, m * m), ("dK", dk, dK, m * m), ("dV", dv, dV, 1.0)):
         bound = _back_rotated(bounds[name], m) if name in ("dQ", "dK") else bounds[name]
         _check(name, _np(got), want, bound, LP_MAX * lp, LP_MEAN * lp)
-    # lse: 1e-3 plus one stored-operand ulp (2^-7 relative in each element of q' and k')
+    # lse: 1e-3 plus one stored-operand ulp in each element of q' and k' (2^-7 relative for
+    # bf16, 2^-10 for f16): the GPU rounds an fp32 rotation, the oracle an fp64 one
+    ulp = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10}[dt]
     pos = np.arange(S)
     qr, kr = rref.rope(q, pos), rref.rope(k, pos)
     e = np.abs(_np(lse) - L)
@@ -195,7 +206,7 @@ def test_rope_random_shapes(shp, seed):
         for h in range(H):
             a = np.abs(qr[b, h]) @ np.abs(kr[b, h // (H // G)]).T
             vis = ref.visible(pos[:, None], pos[None, :], causal, W, NS)
-            bound = LSE_MAX + w.scale * 2.0 * 2.0 ** -7 * np.where(vis, a, 0.0).max(axis=1)
+            bound = LSE_MAX + w.scale * 2.0 * ulp * np.where(vis, a, 0.0).max(axis=1)
             assert (e[b, h] <= bound).all()
 
 
