@@ -231,3 +231,23 @@ def test_fp8_random_shapes(shp, seed):
             tol = hu @ np.abs(vv) + U16 * np.abs(O) + 1e-4
             assert (np.abs(_np(o[b, h]) - O) <= tol).all()
             assert np.abs(_np(lse[b, h]) - L).max() <= LSE_MAX
+
+
+@settings(max_examples=16, **SETTINGS)
+@given(shp=shapes(), dt=st.sampled_from(["bf16", "f16"]), seed=st.integers(0, 10 ** 6))
+def test_grads_one_launch_equals_two(shp, dt, seed):
+    # gqa_attn_bwd_grads runs dK/dV and dQ in one launch when they fit one round (always
+    # at these sizes); it must equal, bit for bit, the two passes launched one after another
+    B, H, G, S, causal, W, NS = shp
+    w = Workload("prop_grads", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, dtype=dt,
+                 direction="fwd+bwd", seed=seed)
+    print(f"[prop] {w}", flush=True)
+    q, k, v, do = (t.cuda() for t in make_inputs(w))
+    kw = dict(causal=causal, window=W, num_sinks=NS)
+    o, lse, o_lo = gqa.gqa_attn_fwd(q, k, v, keep_residual=True, **kw)
+    delta = gqa.gqa_attn_bwd_preprocess(o, do, o_lo=o_lo)
+    dq, dk, dv = gqa.gqa_attn_bwd_grads(q, k, v, lse, do, delta, **kw)
+    dk2, dv2 = gqa.gqa_attn_bwd_dkdv(q, k, v, lse, do, delta, **kw)
+    dq2 = gqa.gqa_attn_bwd_dq(q, k, v, lse, do, delta, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
