@@ -251,3 +251,33 @@ def test_grads_one_launch_equals_two(shp, dt, seed):
     dq2 = gqa.gqa_attn_bwd_dq(q, k, v, lse, do, delta, **kw)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+@settings(max_examples=12, **SETTINGS)
+@given(shp=shapes(), seed=st.integers(0, 10 ** 6))
+def test_every_entry_point_is_deterministic(shp, seed):
+    # no atomics and fixed reduction orders: a second call gives the same bits
+    B, H, G, S, causal, W, NS = shp
+    w = Workload("prop_det", B=B, H=H, G=G, S=S, causal=causal, window=W, num_sinks=NS, direction="fwd+bwd",
+                 seed=seed)
+    print(f"[prop] {w}", flush=True)
+    q, k, v, do = (t.cuda() for t in make_inputs(w))
+    kw = dict(causal=causal, window=W, num_sinks=NS)
+    q8, k8, v8, sc = make_fp8_inputs(w)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+
+    def run():
+        o, lse, o_lo = gqa.gqa_attn_fwd(q, k, v, keep_residual=True, **kw)
+        grads = gqa.gqa_attn_bwd(q, k, v, o, lse, do, o_lo=o_lo, **kw)
+        rope = gqa.gqa_attn_fwd_rope(q, k, v, **kw)
+        fp8 = gqa.gqa_attn_fwd_fp8(q8, k8, v8, *sc, **kw)
+        outs = [o, lse, o_lo, *grads, *rope, *fp8]
+        if causal:  # the last min(S, 8) rows as decode against the whole sequence
+            sq = min(S, 8)
+            outs += gqa.gqa_attn_decode(q[:, :, S - sq:].contiguous(), k, v, window=W, num_sinks=NS)
+        torch.cuda.synchronize()
+        return outs
+
+    first, second = run(), run()
+    for i, (a, b) in enumerate(zip(first, second)):
+        assert torch.equal(a, b), f"output {i} differs between two identical calls"
