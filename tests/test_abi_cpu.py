@@ -363,3 +363,21 @@ def test_outputs_overlapping_inputs_or_outputs_are_rejected():
         assert lib.gqa_attn_bwd_rope(P, r, qr, kr, v, o, olo, lse, do, dq, dk, dv, ws, big, None) == H
         assert lib.gqa_attn_fwd_fp8(P, sc, q, k, v, o, lse, ws, big, None) == H
         assert lib.gqa_attn_decode(D, q, k, v, o, lse, ws, big, None) == H
+
+
+def test_header_serves_a_plain_c_caller(tmp_path):
+    # include/gqa.h compiled as C99 with warnings as errors, linked against the built library
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.join(ROOT, "transformer_attention_07_amd")
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", exe, "-L", lib_dir, "-lgqa",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "status GQA_ERR_INVALID_ARG" in r.stdout
