@@ -1,11 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the fused causal grouped-query attention hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of seeded synthetic inputs
-already resident in HBM: the forward (O, lse), then the backward (delta, then
-dK/dV and dQ through gqa_attn_bwd_grads: one fused launch at the default
-workload) for an upstream gradient dO.  The default workload is the causal
-GQA shape B=4, H=32 query heads, G=8 kv heads, S=2048, d=64, bf16.
+The default line ("headline") measures the path at the model card's attention
+shapes, with seeded synthetic inputs already resident in HBM:
+  * the forward at the card's head layout (128 query heads over 16 kv heads, d=64)
+    with a 16,384-key sliding window and 2,048 sinks at S=65,536, B=1: the largest
+    single-GPU workload, whose throughput is the line's ``value``;
+  * the plain causal forward at the same head layout, S=16,384;
+  * the backward (delta, dK/dV, dQ; each kernel timed on its own) at B=4, H=32,
+    G=8, S=4096, from the forward's O and lse.
+Each kernel carries its own roofline record; the dominant one (the windowed
+forward) is the line's ``roofline``.  Other workloads: ``--workload``; ``step``
+is one forward + backward pass at B=4 H=32 G=8 S=2048.
 
 Work is counted only on visible (query, key) pairs: forward 4*d*pairs*B*H flop
 (Q K^T and P V), backward 10*d*pairs*B*H flop (S, dP, dV, dK, dQ), where the
@@ -14,9 +20,14 @@ carries the step throughput, a roofline record for the dominant kernel (timed
 with HIP events on the stream the kernels run on) and the CPU fp64 oracle
 timed on a bounded sample of the same work on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--rope | --fp8]
-                       [--workload step|c2|c3|c4|c5|long|decode|decode16|rope_k]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--rope | --fp8]
+                       [--workload headline|step|c2|c3|c4|c5|long|decode|decode16|rope_k]
                        [--no-cpu-baseline]
+Every workload also warms up for at least WARMUP_FLOOR_S seconds of GPU work,
+whatever --warmup says: the device settles at its sustained clocks only after
+that.  Counter summaries: --reduce-counters (HBM bytes), --reduce-sq-counters
+(matrix-core busy and issue statistics), --reduce-kernel-trace (per-kernel
+durations, split by launch shape).
 """
 
 from __future__ import annotations
@@ -36,6 +47,9 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (publishe
 MFMA_FP8_PEAK_TFLOPS = 5033.2   # twice the bf16 rate (published 5.0 PFLOP/s dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal GQA attention TFLOP/s (fwd, bwd) at d=64 + % of MI355X bf16 MFMA peak"
+WARMUP_FLOOR_S = 1.0  # seconds of GPU work before any timed step
+N_SIMDS = 256 * 4     # MI355X: 256 compute units of 4 SIMDs
+N_XCDS = 8
 KERNEL_SOURCES = ["gqa_fwd.hip", "gqa_bwd.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_fwd_fp8.hip",
                   "gqa_device.h", "gqa_internal.h"]
 
@@ -48,8 +62,8 @@ def parse_args():
     # whose step takes seconds)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="step",
-                    choices=["step", "c2", "c3", "c4", "c5", "long", "decode", "decode16", "rope_k"])
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "step", "c2", "c3", "c4", "c5", "long", "decode", "decode16", "rope_k"])
     ap.add_argument("--rope", action="store_true",
                     help="YaRN RoPE (factor 32) on q and k in front of attention: rotation of K, the "
                          "forward with Q rotated in registers, and dQ / dK rotated back after the backward")
@@ -62,6 +76,12 @@ def parse_args():
     ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of --workload, then exit")
+    ap.add_argument("--reduce-sq-counters", metavar="SQ_CSV",
+                    help="write profiles/counters.json (and print a summary) from a rocprofv3 --pmc "
+                         "counter_collection.csv with the SQ counters of SQ_COUNTERS for --workload, then exit")
+    ap.add_argument("--reduce-kernel-trace", metavar="TRACE_CSV",
+                    help="print per-kernel duration statistics, split by launch shape, from a rocprofv3 "
+                         "--kernel-trace kernel_trace.csv, then exit")
     return ap.parse_args()
 
 
@@ -153,6 +173,141 @@ def reduce_counters(fetch_csv, write_csv, wname, path=None):
     print(json.dumps(rec["kernels"], indent=1))
 
 
+SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+               "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+               "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+
+
+def _kernel_key(name):
+    return next((v for k, v in KERNEL_KEYS.items() if k in name), None)
+
+
+def _dispatch_table(path):
+    """rocprofv3 counter_collection.csv as {dispatch id: (kernel key, {counter: value}, duration ns)}."""
+    import csv
+
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = _kernel_key(r["Kernel_Name"])
+            if key is None:
+                continue
+            d = out.setdefault(r["Dispatch_Id"], [key, {}, None])
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                d[2] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def sq_derived(c, duration_ns=None):
+    """Matrix-core and issue statistics of one dispatch from its SQ counters.  The GRBM
+    counter arrives summed over the XCDs, so the GPU's own cycle count is a 1/N_XCDS of it;
+    the matrix cores were busy SQ_VALU_MFMA_BUSY_CYCLES out of that times N_SIMDS
+    SIMD-cycles.  Each executed bf16 MFMA operation counts 512 flop."""
+    gpu_cycles = c["GRBM_GUI_ACTIVE"] / N_XCDS
+    wave = c["SQ_WAVE_CYCLES"]
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+    d = {"mfma_busy": busy / (gpu_cycles * N_SIMDS),
+         "mfma_flop_executed": c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+         "mfma_coexec_valu": c["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy if busy else 0.0,
+         "valu_active_per_wave_cycle": c["SQ_ACTIVE_INST_VALU"] / wave,
+         "lds_active_per_wave_cycle": c["SQ_ACTIVE_INST_LDS"] / wave,
+         "wait_issue_per_wave_cycle": c["SQ_WAIT_INST_ANY"] / wave,
+         "lds_bank_conflicts": c["SQ_LDS_BANK_CONFLICT"],
+         "gpu_cycles": gpu_cycles}
+    if duration_ns:
+        d["clock_mhz"] = gpu_cycles / (duration_ns * 1e-3)
+        d["duration_us"] = duration_ns * 1e-3
+    return d
+
+
+def reduce_sq_counters(sq_csv, wname, path=None):
+    """profiles/counters.json entries kernel@wname: the mean over a kernel's dispatches of
+    each statistic of ``sq_derived``, recorded with the kernel sources' digest (a bench line
+    reads them only while the sources are unchanged).  Returns a printable summary."""
+    table = _dispatch_table(sq_csv)
+    per = {}
+    for key, cnt, dur in table.values():
+        if key == "copy" or not all(n in cnt for n in SQ_COUNTERS):
+            continue
+        per.setdefault(key, []).append(sq_derived(cnt, dur))
+    path = path or os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_digest") != source_digest():
+        rec = {"kernels": {}}
+    rec.update(source_digest=source_digest(), counters=SQ_COUNTERS,
+               note="mean over a kernel's dispatches; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                    "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); per-wave-cycle ratios over SQ_WAVE_CYCLES")
+    lines = []
+    for key, ds in sorted(per.items()):
+        mean = {k: sum(d[k] for d in ds) / len(ds) for k in ds[0] if all(k in d for d in ds)}
+        ent = {k: round(v, 6) if abs(v) < 1e6 else float(f"{v:.6e}") for k, v in mean.items()}
+        ent["dispatches"] = len(ds)
+        rec["kernels"][f"{key}@{wname}"] = ent
+        lines.append(f"{key}@{wname}: {len(ds)} dispatches; MFMA busy {100 * mean['mfma_busy']:.1f} %, "
+                     f"executed bf16 MFMA flop {mean['mfma_flop_executed']:.4e}, MFMA cycles co-executing "
+                     f"with VALU {mean['mfma_coexec_valu']:.2f}; per wave cycle: VALU active "
+                     f"{mean['valu_active_per_wave_cycle']:.2f}, LDS active {mean['lds_active_per_wave_cycle']:.2f}, "
+                     f"waiting on issue {mean['wait_issue_per_wave_cycle']:.2f}; LDS bank conflicts "
+                     f"{mean['lds_bank_conflicts']:.0f}"
+                     + (f"; {mean['clock_mhz']:.0f} MHz over {mean['duration_us']:.1f} us" if "clock_mhz" in mean else ""))
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return "\n".join(lines)
+
+
+def load_counters(kernel, wname, path=None):
+    """The counters.json entry of kernel@wname if it was taken on the current kernel
+    sources, else None."""
+    path = path or os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("kernels", {}).get(f"{kernel}@{wname}")
+
+
+def reduce_kernel_trace(trace_csv):
+    """Per-kernel duration statistics from a rocprofv3 kernel_trace.csv, one row per kernel
+    and launch shape (workgroups), so that one kernel run at several shapes in one process
+    is reported per shape.  Returns the table as text."""
+    import csv
+
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            grid = int(float(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+            wg = int(float(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1)) or 1
+            dur = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
+            name = _kernel_key(r["Kernel_Name"]) or r["Kernel_Name"][:60]
+            groups.setdefault((name, grid // wg), []).append(dur)
+    rows = [f"{'kernel':<22}{'workgroups':>11}{'calls':>7}{'avg us':>11}{'median us':>11}{'min us':>10}{'max us':>10}"]
+    for (name, nwg), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        ds_sorted = sorted(ds)
+        rows.append(f"{name:<22}{nwg:>11}{len(ds):>7}{sum(ds) / len(ds):>11.1f}{ds_sorted[len(ds) // 2]:>11.1f}"
+                    f"{ds_sorted[0]:>10.1f}{ds_sorted[-1]:>10.1f}")
+    return "\n".join(rows)
+
+
+def row_decomposition(w):
+    """Workgroups of the forward and dQ launches (heads per workgroup as the library picks
+    them: 4, 2 or 1 dividing H/G; one 64-row tile per wave) and of the dK/dV launch
+    (128 keys per workgroup); used to label launches in kernel traces."""
+    hpg = w.H // w.G
+    hpw = 4 if hpg % 4 == 0 else 2 if hpg % 2 == 0 else 1
+    n_qblk = -(-w.S // (64 * (4 // hpw)))
+    return {"fwd": n_qblk * w.B * (w.H // hpw), "bwd_dq": n_qblk * w.B * (w.H // hpw),
+            "bwd_dkdv": -(-w.S // 128) * w.B * w.G}
+
+
 def host_cpu():
     """The host CPU's model name (for the CPU baseline's record)."""
     try:
@@ -167,7 +322,7 @@ def host_cpu():
     return platform.processor() or "unknown CPU"
 
 
-def cpu_baseline(w, inputs, budget_s, rope=False):
+def cpu_baseline(w, inputs, budget_s, rope=False, rows_sample=None):
     """The oracle, as it stands, on whole kv groups of the same workload until the
     time budget is used: forward rows of every head of the group plus its backward.
     At the long-context workload one group alone would take hours, so there it times
@@ -182,7 +337,9 @@ def cpu_baseline(w, inputs, budget_s, rope=False):
         import oracle.rope as ref  # the same entry points, with the rotation in front
 
     q, k, v, do = inputs
-    if w.per_slab:
+    if rows_sample is None:
+        rows_sample = w.per_slab
+    if rows_sample:
         kw = dict(scale=w.scale, causal=w.causal, window=w.window, num_sinks=w.num_sinks)
         rng = np.random.default_rng(w.seed)
         t0 = time.perf_counter()
@@ -226,6 +383,164 @@ def cpu_baseline(w, inputs, budget_s, rope=False):
                       f"{'fwd+bwd' if 'bwd' in w.direction else 'fwd'}), {dt:.1f} s, fp64 numpy on {host_cpu()}"}
 
 
+def warm_up(call, steps, floor_s=WARMUP_FLOOR_S):
+    """At least ``steps`` calls and at least ``floor_s`` seconds of wall time with the
+    device synchronised (so the seconds are GPU work, not queued launches).  Returns the
+    number of calls and the seconds spent."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < floor_s:
+        call()
+        n += 1
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def time_units(units, steps, stream):
+    """Time ``steps`` passes over ``units`` (a list of callables run in order on
+    ``stream``): per-unit mean milliseconds from HIP events recorded on that stream, and
+    the wall-clock milliseconds per pass between device synchronisations."""
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(units) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, u in enumerate(units):
+            u()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps for i in range(len(units))]
+    return per, wall_ms
+
+
+def kernel_record(kernel, wname, ms, flop=None, nbytes=None):
+    """One kernel's entry of a bench line: its event-timed milliseconds, its rate against
+    its roofline (bf16 MFMA for the attention products, HBM for the delta pass), and what
+    the committed counter summaries say about it (null once the sources have changed)."""
+    traffic = load_traffic(kernel, wname)
+    ctr = load_counters(kernel, wname)
+    d = {"ms": round(ms, 5)}
+    if flop:
+        ach = flop / (ms * 1e-3) / 1e12
+        d.update(tflops=round(ach, 1), pct_peak=round(100 * ach / MFMA_BF16_PEAK_TFLOPS, 2))
+        rf = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        d.update(gbs=round(ach, 1), pct_peak=round(100 * ach / HBM_PEAK_GBS, 2))
+        rf = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(ach / HBM_PEAK_GBS, 4)}
+    rf["traffic"] = traffic
+    rf["hbm_gbs"] = round(traffic / (ms * 1e-3) / 1e9, 1) if traffic else None
+    rf["mfma_busy"] = round(ctr["mfma_busy"], 4) if ctr else None
+    d["roofline"] = rf
+    return d
+
+
+def run_headline(args):
+    """The default line: the windowed forward at S=65,536 (value), the causal forward at
+    S=16,384 and the backward at B=4 H=32 S=4096, each kernel with its own roofline."""
+    import torch
+
+    import transformer_attention_07_amd as gqa
+    from synth import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    kernels, notes = {}, {}
+
+    def fwd_unit(w):
+        print(f"[bench] {w}", file=sys.stderr, flush=True)
+        q, k, v, _ = make_inputs(w, with_do=False)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        kw = dict(causal=w.causal, window=w.window, num_sinks=w.num_sinks, scale=w.scale)
+        call = lambda: gqa.gqa_attn_fwd(qd, kd, vd, out=o, lse=lse, stream=stream, **kw)  # noqa: E731
+        n, secs = warm_up(call, args.warmup)
+        (ms,), wall = time_units([call], args.steps, stream)
+        pairs = gqa.gqa_visible_pairs(w.S, w.causal, w.window, w.num_sinks)
+        flop = 4.0 * w.D * pairs * w.B * w.H
+        notes[w.name] = {"warmup_calls": n, "warmup_s": round(secs, 2)}
+        kernels[f"fwd@{w.name}"] = kernel_record("fwd", w.name, ms, flop=flop)
+        kernels[f"fwd@{w.name}"]["workgroups"] = row_decomposition(w)["fwd"]
+        return (q, k, v), flop, wall
+
+    c4 = WORKLOADS["c4"]
+    c4_inputs, c4_flop, c4_wall = fwd_unit(c4)
+    fwd_unit(WORKLOADS["c3"])
+
+    w5 = WORKLOADS["c5"]
+    print(f"[bench] {w5}", file=sys.stderr, flush=True)
+    q, k, v, do = make_inputs(w5, with_do=True)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    kw = dict(causal=w5.causal, window=w5.window, num_sinks=w5.num_sinks, scale=w5.scale)
+    o, lse, o_lo = gqa.gqa_attn_fwd(qd, kd, vd, keep_residual=True, stream=stream, **kw)  # as in training
+    delta = torch.empty_like(lse)
+    dq = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    units = [lambda: gqa.gqa_attn_bwd_preprocess(o, dod, delta=delta, o_lo=o_lo, stream=stream),
+             lambda: gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta, dk=dk, dv=dv, stream=stream, **kw),
+             lambda: gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta, dq=dq, stream=stream, **kw)]
+    n, secs = warm_up(lambda: [u() for u in units], args.warmup)
+    notes["c5"] = {"warmup_calls": n, "warmup_s": round(secs, 2)}
+    (ms_pre, ms_dkdv, ms_dq), _ = time_units(units, args.steps, stream)
+    clock_mhz = gqa.gqa_clock_probe()  # right after the timed steps, the device still warm
+
+    pairs5 = gqa.gqa_visible_pairs(w5.S, True, 0, 0)
+    bh5 = w5.B * w5.H
+    shapes5 = row_decomposition(w5)
+    kernels["bwd_preprocess@c5"] = kernel_record("bwd_preprocess", "c5", ms_pre,
+                                                 nbytes=3.0 * bh5 * w5.S * w5.D * 2 + bh5 * w5.S * 4)
+    kernels["bwd_dkdv@c5"] = kernel_record("bwd_dkdv", "c5", ms_dkdv, flop=8.0 * w5.D * pairs5 * bh5)
+    kernels["bwd_dkdv@c5"]["workgroups"] = shapes5["bwd_dkdv"]
+    kernels["bwd_dq@c5"] = kernel_record("bwd_dq", "c5", ms_dq, flop=2.0 * w5.D * pairs5 * bh5)
+    kernels["bwd_dq@c5"]["workgroups"] = shapes5["bwd_dq"]
+    bwd_ms = ms_pre + ms_dkdv + ms_dq
+    bwd_t = 10.0 * w5.D * pairs5 * bh5 / (bwd_ms * 1e-3) / 1e12
+    kernels["bwd@c5"] = {"ms": round(bwd_ms, 5), "tflops": round(bwd_t, 1),
+                         "pct_peak": round(100 * bwd_t / MFMA_BF16_PEAK_TFLOPS, 2),
+                         "note": "delta + dK/dV + dQ; 10*d*pairs*B*H flop (S, dP, dV, dK, dQ)"}
+
+    value = c4_flop / (c4_wall * 1e-3) / 1e12
+    dom = kernels["fwd@c4"]
+    roofline = dict(dom["roofline"], kernel="fwd@c4 (fwd_mfma_kernel)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(c4, (*c4_inputs, None), args.cpu_seconds, rows_sample=True)
+
+    pairs4 = gqa.gqa_visible_pairs(c4.S, True, c4.window, c4.num_sinks)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(c4_wall, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": f"causal GQA fwd with sliding window + sinks, B={c4.B} H={c4.H} G={c4.G} "
+                               f"S={c4.S} d={c4.D} window={c4.window} sinks={c4.num_sinks}, bf16 "
+                               "(the model card's head layout; the largest single-GPU workload)",
+                   "B": c4.B, "H": c4.H, "G": c4.G, "S": c4.S, "D": c4.D, "causal": True, "window": c4.window,
+                   "num_sinks": c4.num_sinks, "visible_pairs_per_head": pairs4, "flop_per_step": c4_flop,
+                   "parallelism": "none (1 GPU)",
+                   "also_timed": "fwd at B=1 H=128 G=16 S=16384 (causal); bwd at B=4 H=32 G=8 S=4096 (causal)"},
+        "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "mfma_clock_mhz": round(clock_mhz, 1),
+        "pct_of_peak_at_measured_clock": round(100 * value / (MFMA_BF16_PEAK_TFLOPS * clock_mhz / 2400.0), 2),
+        "mfma_busy": roofline["mfma_busy"], "hbm_gbs": roofline["hbm_gbs"],
+        "kernels": kernels, "warmup_detail": notes,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def decode_bytes(w):
     """Algorithmic HBM bytes of one decode call: every cache row visible to at least one of
     the Sq rows, K and V, read once per kv head; Q read and O written once; lse written."""
@@ -262,9 +577,7 @@ def run_decode(args, w):
         gqa.gqa_attn_decode(qd, kd, vd, window=w.window, num_sinks=w.num_sinks, scale=w.scale, out=o, lse=lse,
                             workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(call, args.warmup)
     if args.copy_calibration:  # a plain copy of known size, for counter calibration
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
@@ -329,9 +642,7 @@ def run_rope_k(args):
     x = torch.randn(B, G, S, D, generator=g, device=dev).to(torch.bfloat16)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        gqa.gqa_rope_apply(x, out=y, stream=stream)
-    torch.cuda.synchronize()
+    warm_up(lambda: gqa.gqa_rope_apply(x, out=y, stream=stream), args.warmup)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
@@ -400,9 +711,7 @@ def run_fp8(args, w):
     def call():
         gqa.gqa_attn_fwd_fp8(q8d, k8d, v8d, *sc, out=o, lse=lse, workspace=ws, stream=stream, **kw)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(call, args.warmup)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
@@ -455,6 +764,12 @@ def main():
         print("bench.py runs on exactly one GPU: the attention path is built and measured on a "
               "single MI355X (no collectives, no sharding); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.reduce_kernel_trace:
+        print(reduce_kernel_trace(args.reduce_kernel_trace))
+        return
+    if args.reduce_sq_counters:
+        print(reduce_sq_counters(args.reduce_sq_counters, args.workload))
+        return
     if args.reduce_counters:
         special = args.workload.startswith("decode") or args.workload == "rope_k"
         name = args.workload if special else (workload(args.workload).name + ("_rope" if args.rope else "")
@@ -463,9 +778,20 @@ def main():
         return
     long_step = args.workload == "long"
     if args.steps is None:
-        args.steps = 3 if long_step else 100
+        args.steps = 3 if long_step else 20
     if args.warmup is None:
-        args.warmup = 1 if long_step else 50
+        args.warmup = 1 if long_step else 5
+    if args.workload == "headline":
+        import torch
+
+        import transformer_attention_07_amd as gqa
+
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        gqa.library()  # fail loudly if the HIP library is not built
+        run_headline(args)
+        return
     if args.workload == "rope_k":
         import torch
 
@@ -557,9 +883,7 @@ def main():
             gqa.gqa_attn_bwd_grads(qd, kd, vd, lse, dod, delta, dq=dq, dk=dk, dv=dv, stream=stream, **kw)
             mark(3)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup, floor_s=0.0 if long_step else WARMUP_FLOOR_S)
 
     if args.copy_calibration:  # a plain copy of known size, for counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -133,6 +133,40 @@ def check_gqa_grouping(impl):
     assert np.allclose(dv[0, 0].sum(0), S, rtol=0, atol=1e-12)
 
 
+def check_attention_weights(impl):
+    """The probability tensor itself: the worked example's attention row in closed form;
+    kv head 1 with K = 0 gives heads {2, 3} uniform rows 1/|vis(i)| over the visible set
+    (written as index ranges) while heads {0, 1}, which read kv head 0 with random K, do
+    not; and P V equals the forward's output for every head (T2's grouping, through P)."""
+    with open(os.path.join(GOLDEN, "p5_worked_example.json")) as f:
+        ex = json.load(f)
+    a = 1.0 / math.sqrt(2.0)
+    P = impl.attention_weights(np.array(ex["Q"])[None, None], np.array(ex["K"])[None, None],
+                               scale=1.0 / math.sqrt(ex["d"]), causal=True)
+    p10 = 1.0 / (1.0 + math.exp(a))
+    assert np.allclose(P[0, 0], [[1.0, 0.0], [p10, 1.0 - p10]], rtol=0, atol=1e-12), P[0, 0]
+    rng = _rng(16)
+    for S, W, NS in [(37, 0, 0), (37, 5, 3), (70, 17, 5), (40, 1, 2)]:
+        B, H, G, D = 1, 4, 2, 3
+        q, v = _rand(rng, B, H, S, D), _rand(rng, B, G, S, D)
+        k = _rand(rng, B, G, S, D) * 3.0
+        k[:, 1] = 0.0
+        P = impl.attention_weights(q, k, causal=True, window=W, num_sinks=NS)
+        for i in range(S):
+            want = np.zeros(S)
+            rs = visible_ranges(i, W, NS)
+            n = sum(hi - lo for lo, hi in rs)
+            for lo, hi in rs:
+                want[lo:hi] = 1.0 / n
+            for h in (2, 3):
+                assert np.allclose(P[0, h, i], want, rtol=0, atol=1e-12), (S, W, NS, h, i)
+        for h in (0, 1):  # random keys: some row with several visible keys is far from uniform
+            assert max(float(np.ptp(P[0, h, i][P[0, h, i] > 0])) for i in range(S)) > 0.05, (S, W, NS, h)
+        O, _ = impl.forward(q, k, v, causal=True, window=W, num_sinks=NS)
+        for h in range(H):
+            assert np.allclose(P[0, h] @ v[0, h // 2], O[0, h], rtol=0, atol=1e-12), (S, W, NS, h)
+
+
 # --------------------------------------------------------------------------
 # 3. Mask semantics from the K = 0 closed form: uniform attention over the
 #    visible set, so lse_i = ln |vis(i)| and O_i = mean of the visible V rows.
@@ -362,7 +396,7 @@ def check_grad_identities(impl):
         assert np.allclose(dv2, 3.0 * dv, rtol=0, atol=1e-12)
 
 
-ALL_CHECKS = [check_worked_example, check_rows_sum_to_one, check_token0, check_gqa_grouping,
+ALL_CHECKS = [check_worked_example, check_rows_sum_to_one, check_token0, check_gqa_grouping, check_attention_weights,
               check_k_zero_closed_form, check_special_cases, check_torch_sdpa, check_fd_gradients,
               check_grad_identities, check_sampled_backward_vs_torch, check_decode_vs_torch,
               check_decode_k_zero_closed_form]

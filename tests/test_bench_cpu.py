@@ -61,3 +61,76 @@ def test_committed_traffic_reads_back():
     if rec["source_digest"] != bench.source_digest():
         pytest.skip("counters predate the current kernel sources")
     assert bench.load_traffic("bwd_grads", "step") == rec["kernels"]["bwd_grads@step"]["bytes_per_launch"]
+
+
+SQ_FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+             "End_Timestamp"]
+
+
+def test_sq_counter_reduction(tmp_path):
+    # Two dispatches of the forward.  The GRBM counter is summed over the 8 XCDs: 8e6 means
+    # 1e6 GPU cycles; over 500 us that is 2000 MHz.  The matrix cores were busy 512e6
+    # SIMD-cycles out of 1e6 x 1024: 50 %.  1e9 executed MFMA operations of 512 flop.
+    fwd = "void gqa::(anonymous namespace)::fwd_mfma_kernel<1, false>(gqa::FwdParams)"
+    vals = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e9, "SQ_VALU_MFMA_BUSY_CYCLES": 512e6,
+            "SQ_VALU_MFMA_COEXEC_CYCLES": 128e6, "SQ_WAVE_CYCLES": 4e8, "SQ_ACTIVE_INST_VALU": 1e8,
+            "SQ_ACTIVE_INST_LDS": 2e7, "SQ_WAIT_INST_ANY": 2e8, "SQ_LDS_BANK_CONFLICT": 0.0, "GRBM_GUI_ACTIVE": 8e6}
+    path = tmp_path / "sq.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=SQ_FIELDS)
+        w.writeheader()
+        for d in (1, 2):
+            for name, v in vals.items():
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": fwd, "Grid_Size": 64, "Counter_Name": name,
+                            "Counter_Value": v, "Start_Timestamp": 1000, "End_Timestamp": 1000 + 500_000})
+        # a copy dispatch and a kernel of no interest are ignored
+        w.writerow({"Dispatch_Id": 3, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 64,
+                    "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1, "Start_Timestamp": 0, "End_Timestamp": 1})
+    out = tmp_path / "counters.json"
+    text = bench.reduce_sq_counters(str(path), "wl", path=str(out))
+    rec = json.loads(out.read_text())
+    ent = rec["kernels"]["fwd@wl"]
+    assert ent["dispatches"] == 2
+    assert ent["mfma_busy"] == pytest.approx(0.5)
+    assert ent["mfma_flop_executed"] == pytest.approx(512e9)
+    assert ent["mfma_coexec_valu"] == pytest.approx(0.25)
+    assert ent["valu_active_per_wave_cycle"] == pytest.approx(0.25)
+    assert ent["wait_issue_per_wave_cycle"] == pytest.approx(0.5)
+    assert ent["clock_mhz"] == pytest.approx(2000.0)
+    assert "MFMA busy 50.0 %" in text
+    assert bench.load_counters("fwd", "wl", path=str(out))["mfma_busy"] == pytest.approx(0.5)
+    assert bench.load_counters("fwd", "other", path=str(out)) is None
+    # a stale digest hides the entry from bench lines
+    rec["source_digest"] = "0" * 16
+    out.write_text(json.dumps(rec))
+    assert bench.load_counters("fwd", "wl", path=str(out)) is None
+
+
+def test_kernel_trace_reduction_splits_launch_shapes(tmp_path):
+    # one kernel at two launch shapes (2048 and 32768 workgroups of 256 lanes): one row each
+    fwd = "void gqa::(anonymous namespace)::fwd_mfma_kernel<1, false>(gqa::FwdParams)"
+    path = tmp_path / "kernel_trace.csv"
+    fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for dur_us, wgs in [(100, 2048), (110, 2048), (30000, 32768), (32000, 32768), (31000, 32768)]:
+            w.writerow({"Kernel_Name": fwd, "Grid_Size_X": wgs * 256, "Workgroup_Size_X": 256,
+                        "Start_Timestamp": 0, "End_Timestamp": dur_us * 1000})
+    rows = bench.reduce_kernel_trace(str(path)).splitlines()
+    assert len(rows) == 3
+    big = rows[1].split()
+    assert big[0] == "fwd" and big[1] == "32768" and big[2] == "3" and float(big[3]) == pytest.approx(31000.0)
+    small = rows[2].split()
+    assert small[1] == "2048" and float(small[3]) == pytest.approx(105.0)
+
+
+def test_row_decomposition_labels():
+    # the launch shapes the library picks (4 heads per workgroup when H/G allows, 64 rows
+    # per wave; 128 keys per dK/dV workgroup)
+    from synth import WORKLOADS
+
+    assert bench.row_decomposition(WORKLOADS["c4"])["fwd"] == 1024 * 32
+    assert bench.row_decomposition(WORKLOADS["c3"])["fwd"] == 256 * 32
+    c5 = bench.row_decomposition(WORKLOADS["c5"])
+    assert c5["fwd"] == 64 * 4 * 8 and c5["bwd_dkdv"] == 32 * 4 * 8

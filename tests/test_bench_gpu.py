@@ -19,6 +19,7 @@ FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
 
 CASES = [
     ([], True),                       # the default line, with the CPU baseline
+    (["--workload", "step"], False),
     (["--workload", "c5"], False),
     (["--workload", "c3"], False),
     (["--workload", "decode16"], False),
@@ -48,6 +49,16 @@ def test_bench_line(args, cpu):
     assert "workload" in d["config"]
     rf = d["roofline"]
     assert rf["bound"] in ("mfma", "hbm") and rf["achieved"] > 0 and 0 < rf["frac"] < 1
+    if not args:  # the default line: the windowed forward at S=65536, with the other headline kernels
+        assert d["config"]["S"] == 65536 and d["config"]["window"] == 16384 and d["config"]["num_sinks"] == 2048
+        for k in ("fwd@c4", "fwd@c3", "bwd_preprocess@c5", "bwd_dkdv@c5", "bwd_dq@c5", "bwd@c5"):
+            assert d["kernels"][k]["ms"] > 0, k
+        for k in ("fwd@c4", "fwd@c3", "bwd_dkdv@c5", "bwd_dq@c5"):
+            r = d["kernels"][k]["roofline"]
+            assert r["bound"] == "mfma" and 0 < r["frac"] < 1, k
+        assert d["roofline"]["achieved"] == d["kernels"]["fwd@c4"]["roofline"]["achieved"]
+        assert "mfma_busy" in d and "hbm_gbs" in d
+        assert d["warmup_detail"]["c4"]["warmup_s"] >= 1.0
     if cpu:
         c = d["cpu_baseline"]
         assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]

@@ -116,6 +116,25 @@ def _make_bwd_mutant(kind):
     return backward_group
 
 
+def _make_weights_mutant(kind):
+    # attention_weights with its own index slip: heads interleaved over the kv heads, or the
+    # scale left out
+    def attention_weights(q, k, scale=None, causal=True, window=0, num_sinks=0):
+        q, k = ref._f64(q), ref._f64(k)
+        B, H, S, D = q.shape
+        G = k.shape[1]
+        scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        rows = np.arange(S)
+        P = np.zeros((B, H, S, S))
+        for b in range(B):
+            for h in range(H):
+                g = h % G if kind == "interleaved" else h // (H // G)
+                sc = 1.0 if kind == "no_scale" else scale
+                P[b, h], _ = ref._softmax_rows(ref._scores(q[b, h], k[b, g], rows, sc, causal, window, num_sinks))
+        return P
+    return attention_weights
+
+
 MUTANTS = {
     "kv_head_interleaved": ("kv_head", _mut_kv_interleaved),
     "causal_strict": ("visible", _mut_causal_strict),
@@ -127,6 +146,8 @@ MUTANTS = {
     "lse_base2": ("_softmax_rows", _mut_lse_base2),
     "lse_without_max": ("_softmax_rows", _mut_lse_no_max),
 }
+MUTANTS["weights_kv_interleaved"] = ("attention_weights", _make_weights_mutant("interleaved"))
+MUTANTS["weights_scale_dropped"] = ("attention_weights", _make_weights_mutant("no_scale"))
 for _kind in ["dv_no_transpose", "D_rowsum_dP", "no_D", "dS_sign", "dq_no_scale", "dq_transposed",
               "dk_no_scale", "dk_last_head_only"]:
     MUTANTS["bwd_" + _kind] = ("backward_group", _make_bwd_mutant(_kind))

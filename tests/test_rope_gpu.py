@@ -20,9 +20,12 @@ What is compared, and the bounds:
     a rounding midpoint the two stored operands differ by one ulp (at most 2^-7 relative),
     which on a row with few keys moves lse by up to that amount.
   * against the exact rotation (no rounding of q', k'): the mean abs errors of O, dQ, dK,
-    dV within the same mean bounds, and lse per row within
+    dV within the same mean bounds, lse per row within
     1e-3 + scale * 2 * 2^-8 * max_j sum_c |q'_ic| |k'_jc| (the most that rounding q' and k'
-    to bf16, 2^-8 relative each with its 8-bit significand, can move a score).
+    to bf16, 2^-8 relative each with its 8-bit significand, can move a score), and every
+    element of O, dQ, dK, dV within its stated bound (the GPU against the stored operands)
+    plus the most that storing q' and k' can move it, derived from the exact quantities
+    (see _storage_bounds).
 Small cases are compared in full, the model card's long-context setting on sampled rows,
 keys and identities.
 """
@@ -168,6 +171,69 @@ def _check_lse_exact(got, want, bound):
     assert (err <= tol).all()
 
 
+def _storage_bounds(QR, KR, v, do, w, u):
+    """Per-element bounds on how far the attention outputs move when the exact rotated
+    operands q*, k* (QR, KR, fp64) are replaced by stored ones within relative u of them
+    (|q' - q*| <= u |q*| element by element, and the same for k').
+
+    Scores move by at most D_ij = scale (2u + u^2) sum_c |q*_ic| |k*_jc|.  With Dm_i the
+    row's largest D_ij, the perturbed probabilities satisfy P'_ij / P_ij in
+    [exp(-D_ij - Dm_i), exp(D_ij + Dm_i)], so |P' - P| <= rho P with rho = exp(D + Dm) - 1.
+    Then, with dP = dO V^T (unchanged) and D_i = sum_j P_ij dP_ij:
+      O:  O' - O = (1/Z) sum_j P_j (e^{d_j} - 1)(v_j - O), Z >= e^{-Dm}
+          -> e^{Dm} sum_j P_j (e^{D_j} - 1) |v_j - O|
+      dV: sum over the group's rows of rho P |dO|
+      D:  |D' - D| = |sum_j (P'_j - P_j)(dP_j - D)| <= eps_i = sum_j rho P |dP - D|
+      dS: |dS' - dS| <= rho P |dP - D| + (1 + rho) P eps
+      dQ before the back-rotation: scale sum_j (|dS' - dS| (1 + u) + u P |dP - D|) |k*_j|
+      (dQ = scale sum_j dS_j k_j with k' in place of k*), and dK the same over the group's
+      query rows with |q*_i|; the back-rotation m R^T turns a pair's error (e0, e1) into
+      at most m sqrt(e0^2 + e1^2) per component.
+    Returns (O, dQ, dK, dV) bounds, fp64, shaped like the outputs."""
+    B, H, S, Dh = QR.shape
+    G = KR.shape[1]
+    hpg = H // G
+    m = float(np.sqrt(M2))
+    v64, do64 = np.asarray(v, dtype=np.float64), np.asarray(do, dtype=np.float64)
+    P = ref_attn.attention_weights(QR, KR, scale=w.scale, **_kw(w))
+    vis = ref_attn.visible(np.arange(S)[:, None], np.arange(S)[None, :], w.causal, w.window, w.num_sinks)
+    bO, bQ = np.zeros((B, H, S, Dh)), np.zeros((B, H, S, Dh))
+    bK, bV = np.zeros((B, G, S, Dh)), np.zeros((B, G, S, Dh))
+
+    def back_rotate(e):  # per pair (2p, 2p + 1): m * sqrt(e0^2 + e1^2) on both components
+        r = m * np.sqrt(e[..., 0::2] ** 2 + e[..., 1::2] ** 2)
+        return np.repeat(r, 2, axis=-1)
+
+    for b in range(B):
+        for h in range(H):
+            g = h // hpg
+            q, k, vv, dO, p = QR[b, h], KR[b, g], v64[b, g], do64[b, h], P[b, h]
+            Dl = np.where(vis, w.scale * (2 * u + u * u) * (np.abs(q) @ np.abs(k).T), 0.0)
+            Dm = Dl.max(axis=1, keepdims=True)
+            rho = np.where(vis, np.expm1(Dl + Dm), 0.0)
+            O = p @ vv
+            absdiff = np.abs(vv[None, :, :] - O[:, None, :])            # |v_j - O_i| [i, j, c]
+            bO[b, h] = np.exp(Dm) * np.einsum("ij,ijc->ic", p * np.expm1(Dl), absdiff)
+            bV[b, g] += (rho * p).T @ np.abs(dO)
+            dP = dO @ vv.T
+            dPD = np.abs(dP - (p * dP).sum(axis=1, keepdims=True))
+            eps = (rho * p * dPD).sum(axis=1, keepdims=True)
+            dS_err = rho * p * dPD + (1.0 + rho) * p * eps
+            coef = np.where(vis, dS_err * (1.0 + u) + u * p * dPD, 0.0)
+            bQ[b, h] = back_rotate(w.scale * coef @ np.abs(k))
+            bK[b, g] += w.scale * coef.T @ np.abs(q)
+    bK = back_rotate(bK)
+    return bO, bQ, bK, bV
+
+
+def _max_err_bounded(name, got, want, tol):
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    ratio = float((err / tol).max()) if err.size else 0.0
+    print(f"  {name} vs the exact rotation: max {err.max():.3e} (worst err/bound {ratio:.3f}, "
+          f"bound {float(tol.min()):.2e}..{float(tol.max()):.2e})", flush=True)
+    assert (err <= tol).all(), f"{name}: {int((err > tol).sum())} elements beyond the storage-rounding bound"
+
+
 def _mean_err(name, got, want, mean_tol):
     err = np.abs(np.asarray(got, dtype=np.float64) - want)
     print(f"  {name} vs the exact rotation: max {err.max():.3e} mean {err.mean():.3e}", flush=True)
@@ -224,6 +290,11 @@ def check_rope_full(w: Workload):
     _check_lse_exact(got["lse"], L, bound)
     for name, want, tol in (("O", O, LP_MEAN), ("dQ", dQ, GRAD_MEAN), ("dK", dK, GRAD_MEAN), ("dV", dV, LP_MEAN)):
         _mean_err(name, got[name], want, tol)
+    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
+    bO, bQ, bK, bV = _storage_bounds(QR, KR, v.float().numpy(), do.float().numpy(), w, u)
+    for name, want, stated, extra in (("O", O, LP_MAX, bO), ("dQ", dQ, GRAD_MAX, bQ), ("dK", dK, GRAD_MAX, bK),
+                                      ("dV", dV, LP_MAX, bV)):
+        _max_err_bounded(name, got[name], want, stated + extra)
 
 
 ROPE_SMALL = [

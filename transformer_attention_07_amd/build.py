@@ -65,5 +65,28 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage(src: str) -> dict:
+    """Per-kernel register and scratch usage of one HIP source, compiled for the device
+    only, from the compiler's kernel-resource-usage remarks: {kernel symbol: {"vgprs",
+    "agprs", "sgprs", "scratch_bytes_per_lane", "occupancy"}}."""
+    import re
+
+    cmd = [_hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, "-x", "hip", "--offload-device-only", "-c",
+           os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+    out = _run(cmd, False)
+    fields = {"VGPRs": "vgprs", "AGPRs": "agprs", "TotalSGPRs": "sgprs",
+              "ScratchSize [bytes/lane]": "scratch_bytes_per_lane", "Occupancy [waves/SIMD]": "occupancy"}
+    res, cur = {}, None
+    for line in out.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            cur = res.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*): (\d+)", line)
+        if m and cur is not None and m.group(1).strip() in fields:
+            cur[fields[m.group(1).strip()]] = int(m.group(2))
+    return res
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))

@@ -222,48 +222,13 @@ struct DkdvWave {
   }
 };
 
-// Wave-uniform copies of the parameters (and of the workgroup index): the out-of-line pass
-// receives its arguments in vector registers, and buffer descriptors built from non-uniform values turn every buffer load
-// into a waterfall loop.
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ float uni(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-template <typename T>
-__device__ __forceinline__ T* uni(T* ptr) {
-  const uint64_t v = (uint64_t)ptr;
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return (T*)((hi << 32) | lo);
-}
-// The kernels' second argument (the rotation table) in place in the kernel-argument
-// segment, so that the out-of-line passes read it there instead of taking a copy on each
-// lane's stack.  Only a kernel itself may call this: the segment pointer is not passed on
-// to called functions, which receive the table's address as an argument instead.
-__device__ __forceinline__ const RopeSpec* kernel_rope_arg() {
-  return (const RopeSpec*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + kBwdRopeArgOffset);
-}
-
-__device__ __forceinline__ BwdParams uniform_params(const BwdParams& in) {
-  BwdParams p;
-  p.q = uni(in.q); p.k = uni(in.k); p.v = uni(in.v); p.o = uni(in.o); p.o_lo = uni(in.o_lo);
-  p.d_o = uni(in.d_o); p.lse = uni(in.lse); p.delta = uni(in.delta); p.out_delta = uni(in.out_delta);
-  p.dq = uni(in.dq); p.dk = uni(in.dk); p.dv = uni(in.dv);
-  p.B = uni(in.B); p.H = uni(in.H); p.G = uni(in.G); p.S = uni(in.S);
-  p.scale = uni(in.scale); p.scale_log2 = uni(in.scale_log2);
-  p.mask.S = uni(in.mask.S); p.mask.causal = uni(in.mask.causal);
-  p.mask.window = uni(in.mask.window); p.mask.sinks = uni(in.mask.sinks);
-  p.hpw = uni(in.hpw); p.qpw = uni(in.qpw); p.n_qblk = uni(in.n_qblk); p.n_kblk = uni(in.n_kblk);
-  return p;
-}
-
-// The whole dK/dV pass for one workgroup.  Kept out of line so that the rare variant for
-// key blocks holding sink keys (PRECISE: two products per P and dS) gets its own register
-// allocation instead of raising the common variant's.
+// The whole dK/dV pass for one workgroup.  Every pass is inlined into its kernel: a call
+// to an out-of-line pass makes the callee save the callee-saved vector registers it uses
+// to scratch memory (up to 500 bytes per lane here), while the two variants of a branch
+// share one allocation at the larger variant's pressure.
 template <int DT, bool PRECISE, bool ROPE>
-__device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int wg_in, const RopeSpec* rope) {
-  const BwdParams p = uniform_params(pin);
-  const int wg = uni(wg_in);
+__device__ __forceinline__ void dkdv_block(const BwdArgs& a, int wg) {
+  const BwdParams& p = a.p;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -394,7 +359,7 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
       const int d0 = db * 32 + 8 * r4 + 4 * W.hl;
       f32x4 kv = {W.dk[db][4 * r4] * p.scale, W.dk[db][4 * r4 + 1] * p.scale, W.dk[db][4 * r4 + 2] * p.scale,
                   W.dk[db][4 * r4 + 3] * p.scale};
-      if constexpr (ROPE) kv = rope_back4(kv, j, *rope, d0 / 2);  // gradient of the unrotated K
+      if constexpr (ROPE) kv = rope_back4(kv, j, a.rope, d0 / 2);  // gradient of the unrotated K
       const f32x4 vv = {W.dv[db][4 * r4], W.dv[db][4 * r4 + 1], W.dv[db][4 * r4 + 2], W.dv[db][4 * r4 + 3]};
       *(f32x4*)(dkslab + (size_t)j * kHeadDim + d0) = kv;
       *(f32x4*)(dvslab + (size_t)j * kHeadDim + d0) = vv;
@@ -405,17 +370,17 @@ __device__ __attribute__((noinline)) void dkdv_block(const BwdParams& pin, int w
 // large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value plus
 // its rounded residual (two products each), which keeps their rounding out of the sum.
 template <int DT, bool ROPE>
-__device__ __forceinline__ void dkdv_dispatch(const BwdParams& p, int wg, const RopeSpec* rope) {
-  const int kblk = wg / (p.B * p.G);
-  if (p.mask.window > 0 && kblk * kDkdvKeys < p.mask.sinks)
-    dkdv_block<DT, true, ROPE>(p, wg, rope);
+__device__ __forceinline__ void dkdv_dispatch(const BwdArgs& a, int wg) {
+  const int kblk = wg / (a.p.B * a.p.G);
+  if (a.p.mask.window > 0 && kblk * kDkdvKeys < a.p.mask.sinks)
+    dkdv_block<DT, true, ROPE>(a, wg);
   else
-    dkdv_block<DT, false, ROPE>(p, wg, rope);
+    dkdv_block<DT, false, ROPE>(a, wg);
 }
 
 template <int DT, bool ROPE>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, RopeSpec) {
-  dkdv_dispatch<DT, ROPE>(p, (int)blockIdx.x, ROPE ? kernel_rope_arg() : nullptr);
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  dkdv_dispatch<DT, ROPE>(a, (int)blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------------
@@ -428,7 +393,8 @@ __shared__ __attribute__((aligned(1024))) char g_dq_v0[8192];
 __shared__ __attribute__((aligned(1024))) char g_dq_v1[8192];
 
 template <int DT, bool ROPE>
-__device__ __forceinline__ void dq_body(const BwdParams& p, int wg, const RopeSpec* rope) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int wg) {
+  const BwdParams& p = a.p;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -620,35 +586,29 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int wg, const RopeSp
         const int d0 = db * 32 + 8 * r4 + 4 * hl;
         f32x4 w = {dq[db][cb][4 * r4] * p.scale, dq[db][cb][4 * r4 + 1] * p.scale,
                    dq[db][cb][4 * r4 + 2] * p.scale, dq[db][cb][4 * r4 + 3] * p.scale};
-        if constexpr (ROPE) w = rope_back4(w, i, *rope, d0 / 2);  // gradient of the unrotated Q
+        if constexpr (ROPE) w = rope_back4(w, i, a.rope, d0 / 2);  // gradient of the unrotated Q
         *(f32x4*)(p.dq + (qslab_rows + i) * kHeadDim + d0) = w;
       }
   }
 }
 
 template <int DT, bool ROPE>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, RopeSpec) {
-  dq_body<DT, ROPE>(p, (int)blockIdx.x, ROPE ? kernel_rope_arg() : nullptr);
-}
-
-template <int DT, bool ROPE>
-__device__ __attribute__((noinline)) void dq_block(const BwdParams& pin, int wg, const RopeSpec* rope) {
-  dq_body<DT, ROPE>(uniform_params(pin), uni(wg), rope);
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  dq_body<DT, ROPE>(a, (int)blockIdx.x);
 }
 
 // dK/dV and dQ in one launch: the dK/dV workgroups (heaviest key blocks first) come first,
 // then the dQ workgroups (heaviest query blocks first), so dQ work fills the CUs that the
 // light dK/dV blocks free while the heavy ones still run.  The two passes are independent
-// (both only read Q, K, V, dO, lse, delta) and each keeps its own register allocation.
+// (both only read Q, K, V, dO, lse, delta).
 template <int DT, bool ROPE>
-__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdParams p, RopeSpec) {
-  const int n_dkdv = p.n_kblk * p.B * p.G;
+__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs a) {
+  const int n_dkdv = a.p.n_kblk * a.p.B * a.p.G;
   const int wg = (int)blockIdx.x;
-  const RopeSpec* rope = ROPE ? kernel_rope_arg() : nullptr;
   if (wg < n_dkdv)
-    dkdv_dispatch<DT, ROPE>(p, wg, rope);
+    dkdv_dispatch<DT, ROPE>(a, wg);
   else
-    dq_block<DT, ROPE>(p, wg - n_dkdv, rope);
+    dq_body<DT, ROPE>(a, wg - n_dkdv);
 }
 
 // Kernels by element type and by whether dQ / dK are rotated back at the store.
@@ -680,20 +640,23 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   dim3 grid((unsigned)((long long)p.n_kblk * p.B * p.G)), block(256);
-  void* args[] = {(void*)&p, (void*)&rope};
+  BwdArgs a{p, rope};
+  void* args[] = {(void*)&a};
   return hipLaunchKernel(pick_bwd(0, rope, dtype), grid, block, args, 0, s);
 }
 
 hipError_t launch_bwd_dq_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   dim3 grid((unsigned)((long long)p.n_qblk * p.B * (p.H / p.hpw))), block(256);
-  void* args[] = {(void*)&p, (void*)&rope};
+  BwdArgs a{p, rope};
+  void* args[] = {(void*)&a};
   return hipLaunchKernel(pick_bwd(1, rope, dtype), grid, block, args, 0, s);
 }
 
 hipError_t launch_bwd_fused_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s) {
   const long long n = (long long)p.n_kblk * p.B * p.G + (long long)p.n_qblk * p.B * (p.H / p.hpw);
   dim3 grid((unsigned)n), block(256);
-  void* args[] = {(void*)&p, (void*)&rope};
+  BwdArgs a{p, rope};
+  void* args[] = {(void*)&a};
   return hipLaunchKernel(pick_bwd(2, rope, dtype), grid, block, args, 0, s);
 }
 

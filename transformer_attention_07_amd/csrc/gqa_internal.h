@@ -182,10 +182,13 @@ struct BwdParams {
   int n_kblk;            // dK/dV pass: kDkdvKeys-key blocks per kv head
 };
 
-// The dK/dV and dQ kernels take (BwdParams, RopeSpec); with rope.enabled they rotate dQ and
-// dK back (m R^T at their positions) as they store them.  The second argument starts at
-// this offset of the kernel-argument segment (arguments in order, each at its alignment).
-constexpr size_t kBwdRopeArgOffset = (sizeof(BwdParams) + alignof(RopeSpec) - 1) / alignof(RopeSpec) * alignof(RopeSpec);
+// The only argument of the dK/dV, dQ and one-launch backward kernels: the parameters and
+// the rotation table (with rope.enabled they rotate dQ and dK back, m R^T at their
+// positions, as they store them).  One block, so no argument offset is computed by hand.
+struct BwdArgs {
+  BwdParams p;
+  RopeSpec rope;
+};
 
 // Launchers (return hipSuccess or the launch error).  Element type by dtype code.
 // Decode (few query rows against a key/value cache), split over the visible key tiles.
