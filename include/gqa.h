@@ -66,6 +66,7 @@ extern "C" {
 
 #define GQA_ABI_VERSION 1
 #define GQA_MAX_SEQ (1 << 23) /* longest S / Skv the attention entry points accept */
+#define GQA_NOALLOC_MAX_ROWS (1 << 23) /* largest B * H * S of gqa_attn_bwd_noalloc */
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -132,6 +133,20 @@ size_t gqa_attn_bwd_workspace_bytes(const gqa_problem* p);
 int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v,
                  const void* o, const void* o_lo, const float* lse, const void* d_o, float* dq,
                  float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* gqa_attn_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The workspace (the fp32
+ * delta vector) is a fixed array inside the library, GQA_NOALLOC_MAX_ROWS floats (32 MiB),
+ * which each device the library runs on holds until the process ends; the call allocates
+ * nothing.  Arguments, results (bit-identical to gqa_attn_bwd's) and errors as
+ * gqa_attn_bwd, except: a problem with B * H * S > GQA_NOALLOC_MAX_ROWS returns
+ * GQA_ERR_WORKSPACE before anything is enqueued; the first call on a device looks up the
+ * array's address there (GQA_ERR_HIP if that fails).  Every call on one device shares that
+ * device's array: calls that may overlap on one device (several streams, several host
+ * threads) race on it and must be ordered by the caller. */
+int gqa_attn_bwd_noalloc(const gqa_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const void* o_lo, const float* lse, const void* d_o, float* dq,
+                         float* dk, float* dv, void* stream);
 
 /* Backward step 1: delta[b,h,i] = sum_c dO[b,h,i,c] * (O + o_lo)[b,h,i,c], accumulated in
  * fp32 (o_lo may be NULL). */

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = gqa.library()
     declared = _declared_functions()
-    assert len(declared) == 18, declared
+    assert len(declared) == 19, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(declared) == sorted(binding.EXPORTED)
@@ -37,6 +37,8 @@ def test_header_constants_match_the_binding():
     assert int(re.search(r"#define GQA_ABI_VERSION (\d+)", text).group(1)) == gqa.abi_version()
     shift = int(re.search(r"#define GQA_MAX_SEQ \(1 << (\d+)\)", text).group(1))
     assert binding.GQA_MAX_SEQ == 1 << shift
+    shift = int(re.search(r"#define GQA_NOALLOC_MAX_ROWS \(1 << (\d+)\)", text).group(1))
+    assert binding.GQA_NOALLOC_MAX_ROWS == 1 << shift
     for name, value in re.findall(r"\b(GQA_(?:OK|ERR_\w+)) = (\d+)", text):
         assert getattr(binding, name) == int(value), name
     for name, value in re.findall(r"\b(GQA_(?:F32|BF16|F16)) = (\d+)", text):
@@ -128,6 +130,31 @@ def test_bwd_validation_and_workspace():
     assert lib.gqa_attn_bwd_workspace_bytes(ctypes.byref(long_p)) == 0
     assert lib.gqa_attn_bwd(ctypes.byref(long_p), *([FAKE] * 10), FAKE, 1 << 40, None) == binding.GQA_ERR_UNSUPPORTED
     assert lib.gqa_attn_bwd_grads(ctypes.byref(long_p), *([FAKE] * 9), None) == binding.GQA_ERR_UNSUPPORTED
+
+
+def test_bwd_noalloc_validation():
+    # the allocation-free backward: gqa_attn_bwd's checks, and problems whose delta vector
+    # does not fit the library's fixed scratch refused with GQA_ERR_WORKSPACE, all before
+    # any HIP call
+    lib = gqa.library()
+    q, k, v, o, olo, lse, do, dq, dk, dv = (FAKE + i * (1 << 34) for i in range(10))
+    ok = gqa.make_problem(1, 4, 2, 128)
+    assert lib.gqa_attn_bwd_noalloc(ctypes.byref(gqa.make_problem(1, 4, 3, 128)), q, k, v, o, olo, lse, do, dq,
+                                    dk, dv, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_noalloc(ctypes.byref(ok), q, k, v, o, olo, lse, do, q, dk, dv, None) \
+        == binding.GQA_ERR_INVALID_ARG                                    # dQ over Q
+    assert lib.gqa_attn_bwd_noalloc(ctypes.byref(ok), q, k, None, o, olo, lse, do, dq, dk, dv, None) \
+        == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_attn_bwd_noalloc(ctypes.byref(gqa.make_problem(0, 4, 2, 128)), *([None] * 10), None) \
+        == binding.GQA_OK                                                 # empty: no-op
+    rows = binding.GQA_NOALLOC_MAX_ROWS
+    fits, over = gqa.make_problem(1, 128, 16, rows // 128), gqa.make_problem(1, 128, 16, rows // 128 + 1)
+    assert lib.gqa_attn_bwd_noalloc(ctypes.byref(over), q, k, v, o, olo, lse, do, dq, dk, dv, None) \
+        == binding.GQA_ERR_WORKSPACE
+    import torch
+    if torch.cuda.device_count() == 0:  # valid: fails only at the device lookup (fake pointers)
+        assert lib.gqa_attn_bwd_noalloc(ctypes.byref(fits), q, k, v, o, olo, lse, do, dq, dk, dv, None) \
+            == binding.GQA_ERR_HIP
 
 
 def _dec(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):

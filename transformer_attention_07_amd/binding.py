@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so"
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 GQA_MAX_SEQ = 1 << 23   # longest S / Skv the attention entry points accept
+GQA_NOALLOC_MAX_ROWS = 1 << 23   # largest B * H * S of gqa_attn_bwd_noalloc
 _DTYPES = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16, torch.float16: GQA_F16}
 
 EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_fwd",
@@ -29,7 +30,7 @@ EXPORTED = ("gqa_abi_version", "gqa_status_str", "gqa_visible_pairs", "gqa_attn_
             "gqa_attn_bwd_dkdv", "gqa_attn_bwd_dq", "gqa_attn_bwd_grads",
             "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_rope_apply",
             "gqa_attn_fwd_rope", "gqa_attn_bwd_rope", "gqa_attn_fwd_fp8_workspace_bytes", "gqa_attn_fwd_fp8",
-            "gqa_clock_probe")
+            "gqa_clock_probe", "gqa_attn_bwd_noalloc")
 
 
 class GqaError(RuntimeError):
@@ -104,6 +105,8 @@ def library() -> ctypes.CDLL:
     lib.gqa_attn_bwd_workspace_bytes.argtypes = [P]
     lib.gqa_attn_bwd.restype = ctypes.c_int
     lib.gqa_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.gqa_attn_bwd_noalloc.restype = ctypes.c_int
+    lib.gqa_attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, vp]
     lib.gqa_attn_bwd_preprocess.restype = ctypes.c_int
     lib.gqa_attn_bwd_preprocess.argtypes = [P, vp, vp, vp, fp, vp]
     lib.gqa_attn_bwd_dkdv.restype = ctypes.c_int
@@ -275,6 +278,22 @@ def gqa_attn_bwd(q, k, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale
     _run(q.device, "gqa_attn_bwd", library().gqa_attn_bwd,
          ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
          _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    return dq, dk, dv
+
+
+def gqa_attn_bwd_noalloc(q, k, v, o, lse, d_o, causal=True, window=0, num_sinks=0, scale=None, dq=None,
+                         dk=None, dv=None, stream=None, o_lo=None):
+    """gqa_attn_bwd without a workspace argument: the library's own fixed scratch holds
+    delta (B*H*S <= GQA_NOALLOC_MAX_ROWS).  The C call allocates nothing; this wrapper
+    only allocates dq, dk, dv when they are not given."""
+    p = _problem_from(q, k, causal, window, num_sinks, scale)
+    _check_bwd_inputs(q, k, v, o, lse, d_o)
+    if o_lo is not None:
+        _need(o_lo, "o_lo", dtype=q.dtype, shape=q.shape, device=q.device)
+    dq, dk, dv = _grad_buffers(q, k, dq, dk, dv)
+    _run(q.device, "gqa_attn_bwd_noalloc", library().gqa_attn_bwd_noalloc,
+         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
+         _ptr(dv), _stream(stream, q.device))
     return dq, dk, dv
 
 

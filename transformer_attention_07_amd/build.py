@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
 
-SOURCES = ["gqa_api.cpp", "gqa_fwd.hip", "gqa_bwd.hip", "gqa_f32.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_fwd_fp8.hip", "gqa_clock.hip"]
+SOURCES = ["gqa_api.cpp", "gqa_fwd.hip", "gqa_bwd.hip", "gqa_f32.hip", "gqa_decode.hip", "gqa_rope.hip", "gqa_fwd_fp8.hip", "gqa_clock.hip",
+           "gqa_noalloc.hip"]
 ARCH = os.environ.get("GQA_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.

@@ -514,22 +514,43 @@ int gqa_attn_bwd_grads(const gqa_problem* p, const void* q, const void* k, const
   return run_grads(p, q, k, v, lse, d_o, delta, dq, dk, dv, nullptr, stream);
 }
 
-int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
-                 const void* o_lo, const float* lse, const void* d_o, float* dq, float* dk, float* dv,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_problem(p);
+}  // extern "C"
+
+namespace gqa {
+
+// gqa_attn_bwd's argument checks, in its order: the problem, the pointers, the workspace
+// (unless own_workspace: the caller brings none), then overlaps.
+int bwd_check_args(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
+                   const void* o_lo, const float* lse, const void* d_o, const float* dq, const float* dk,
+                   const float* dv, bool own_workspace, const void* workspace, size_t workspace_bytes) {
+  const int rc = check_problem(p);
   if (rc != GQA_OK) return rc;
   if (empty_problem(p)) return GQA_OK;
   if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(d_o) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return GQA_ERR_INVALID_ARG;
-  if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+  if (!own_workspace) {
+    if (workspace == nullptr || workspace_bytes < gqa_attn_bwd_workspace_bytes(p)) return GQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GQA_ERR_INVALID_ARG;
+  }
   const Sizes z = sizes_of(p);
-  if (aliased({{dq, z.q32}, {dk, z.kv32}, {dv, z.kv32}, {workspace, z.row}},
+  if (aliased({{dq, z.q32}, {dk, z.kv32}, {dv, z.kv32}, {own_workspace ? nullptr : workspace, z.row}},
               {{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {o_lo, z.q}, {lse, z.row}, {d_o, z.q}}))
     return GQA_ERR_INVALID_ARG;
+  if (o_lo != nullptr && (p->dtype == GQA_F32 || !aligned16(o_lo))) return GQA_ERR_INVALID_ARG;
+  return GQA_OK;
+}
+
+}  // namespace gqa
+
+extern "C" {
+
+int gqa_attn_bwd(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
+                 const void* o_lo, const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gqa::bwd_check_args(p, q, k, v, o, o_lo, lse, d_o, dq, dk, dv, false, workspace, workspace_bytes);
+  if (rc != GQA_OK || empty_problem(p)) return rc;
   BwdParams bp;
   if ((rc = fill_bwd(p, &bp)) != GQA_OK) return rc;
   float* delta = (float*)workspace;

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gqa.h"
+
 namespace gqa {
 
 constexpr int kTile = 64;   // keys per key tile and query rows per wave tile
@@ -253,6 +255,12 @@ hipError_t launch_rope(const RopeParams& p, int dtype, hipStream_t s);
 int rope_rows_per_block(int dtype);
 
 hipError_t launch_fwd_mfma(const FwdParams& p, int dtype, hipStream_t s);
+
+// Host side: gqa_attn_bwd's argument checks (GQA_OK for a valid or empty problem); with
+// own_workspace the workspace is the library's and is not checked.
+int bwd_check_args(const gqa_problem* p, const void* q, const void* k, const void* v, const void* o,
+                   const void* o_lo, const float* lse, const void* d_o, const float* dq, const float* dk,
+                   const float* dv, bool own_workspace, const void* workspace, size_t workspace_bytes);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_dkdv_mfma(const BwdParams& p, const RopeSpec& rope, int dtype, hipStream_t s);
