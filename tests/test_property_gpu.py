@@ -3,9 +3,13 @@
 through the C-ABI against the CPU fp64 oracle, for the forward + backward (bf16, f16 and
 fp32), decode (bf16 and f16), the RoPE path (bf16, f16 and fp32) and the FP8 forward.
 
-Bounds.  fp32: 1e-4 max abs on everything.  16-bit: each element within the larger of the
-stated 2e-2 and the most the kernels' own roundings can move it, the mean within the
-larger of 2e-3 and twice the expected size of those roundings (lse: 1e-3).  The kernels
+Bounds.  fp32: 1e-4 max abs on everything.  16-bit forward + backward: the stated 2e-2 max
+and 2e-3 mean abs on O, dQ, dK, dV and 1e-3 on lse, as for the named workloads (the
+backward keeps P's and dS's rounding residuals where each query sees few keys, which is
+where rounding P alone would exceed the mean bar).  16-bit RoPE: each element within the
+larger of the stated bounds and the most the kernels' own roundings of the stored operands
+can move it, the mean within the larger of 2e-3 and twice the expected size of those
+roundings (lse: 1e-3).  The kernels
 round to the element type exactly the factors they hand to the matrix cores: P before P V
 (forward) and P^T dO (dV), dS before dS K (dQ) and dS^T Q (dK), and O on output; each
 rounding moves a value x by at most u |x|, u = 2^-8 for bf16 (8-bit significand) and
@@ -140,10 +144,10 @@ def test_fwd_bwd_random_shapes(shp, dt, seed):
             assert _err(_np(got[name]), want[name])[0] <= 1e-4, name
         assert _err(_np(lse), L)[0] <= 1e-4
         return
-    f64 = [ref._f64(x) for x in (q, k, v, do)]
-    bounds = _rounding_bounds(*f64, O, w.scale, causal, W, NS, UNIT_ROUNDOFF[dt])
+    # the stated bf16 bar, as for the named workloads
     for name in got:
-        _check(name, _np(got[name]), want[name], bounds[name], LP_MAX, LP_MEAN)
+        mx, mean = _err(_np(got[name]), want[name])
+        assert mx <= LP_MAX and mean <= LP_MEAN, (name, mx, mean)
     assert _err(_np(lse), L)[0] <= LSE_MAX
 
 

@@ -17,6 +17,10 @@ using gqa::FwdParams;
 using gqa::MaskSpec;
 
 constexpr float kLog2e = 1.44269504088896340736f;
+// The dK/dV pass takes P and dS with their rounding residuals in every block for sequences
+// up to this length or windows up to this width (see BwdParams::precise_all).
+constexpr int kPreciseMaxSeq = 256;
+constexpr int kPreciseMaxWindow = 64;
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -63,6 +67,27 @@ void row_decomposition(const gqa_problem* p, int* hpw, int* qpw, int* n_qblk) {
 
 int grid_ok(long long blocks) { return blocks > 0 && blocks <= INT_MAX; }
 
+int current_cu_count();
+
+// Workgroup order of the 16-bit forward (the kernel's fwd_block_order).  Workgroup j runs
+// on XCD j mod 8, each XCD with its own L2.  When the head groups (B * H / hpw) split into
+// eight equal shares of whole kv heads, each XCD serves one share, so a kv head's K/V tiles
+// stay in one L2; and when one kv head's workgroups fill at least four rounds of an XCD's
+// workgroup slots (two per CU), the XCD finishes each kv head before starting the next,
+// which holds a single kv head's tiles per L2 at a time (on smaller grids that order
+// would leave light row blocks of one kv head ahead of heavy ones of the next).
+void xcd_block_order(const gqa_problem* p, int hpw, int n_qblk, int* xcd_hg, int* xcd_kv) {
+  *xcd_hg = 0;
+  *xcd_kv = 0;
+  const long long nhg = (long long)p->B * (p->H / hpw);
+  const int per_kv = (p->H / p->G) / hpw;  // head groups of one kv head
+  if (nhg % 8 != 0 || (nhg / 8) % per_kv != 0) return;
+  *xcd_hg = (int)(nhg / 8);
+  const int cus = current_cu_count();
+  const long long slots_per_xcd = cus > 0 ? 2LL * cus / 8 : 64;
+  if ((long long)n_qblk * per_kv >= 4 * slots_per_xcd) *xcd_kv = per_kv;
+}
+
 // Compute units of the current device (cached per device; 0 if the query fails).
 int current_cu_count() {
   static std::atomic<int> cached[64] = {};  // calls may come from several host threads
@@ -89,6 +114,8 @@ int fill_bwd(const gqa_problem* p, BwdParams* bp) {
   bp->mask = normalised_mask(p);
   row_decomposition(p, &bp->hpw, &bp->qpw, &bp->n_qblk);
   bp->n_kblk = (p->S + gqa::kDkdvKeys - 1) / gqa::kDkdvKeys;
+  // few keys per query: large P, whose rounding a key's dV and dK would not average out
+  bp->precise_all = (p->S <= kPreciseMaxSeq || (bp->mask.window > 0 && bp->mask.window <= kPreciseMaxWindow)) ? 1 : 0;
   if (!grid_ok((long long)bp->n_qblk * p->B * (p->H / bp->hpw))) return GQA_ERR_UNSUPPORTED;
   if (!grid_ok((long long)bp->n_kblk * p->B * p->G)) return GQA_ERR_UNSUPPORTED;
   if (!grid_ok((long long)p->B * p->H * ((p->S + 63) / 64))) return GQA_ERR_UNSUPPORTED;
@@ -272,6 +299,7 @@ int run_fwd(const gqa_problem* p, const void* q, const void* k, const void* v, v
   fp.scale_log2 = p->scale * kLog2e;
   fp.mask = normalised_mask(p);
   row_decomposition(p, &fp.hpw, &fp.qpw, &fp.n_qblk);
+  xcd_block_order(p, fp.hpw, fp.n_qblk, &fp.xcd_hg, &fp.xcd_kv);
   if (rope != nullptr) {
     fp.rope = *rope;
     fp.q_rot = q_rot;

@@ -369,10 +369,13 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, int wg) {
 // Sink keys collect attention from every later query, so their dK and dV are sums of many
 // large terms: in blocks holding sinks, P and dS enter the MFMAs as a rounded value plus
 // its rounded residual (two products each), which keeps their rounding out of the sum.
+// The same holds for every block when each query sees only a few keys (short sequences,
+// short windows): then P is large and a key's dV sums few such terms per head, so the
+// rounding of P would not average out (precise_all, set by the host).
 template <int DT, bool ROPE>
 __device__ __forceinline__ void dkdv_dispatch(const BwdArgs& a, int wg) {
   const int kblk = wg / (a.p.B * a.p.G);
-  if (a.p.mask.window > 0 && kblk * kDkdvKeys < a.p.mask.sinks)
+  if (a.p.precise_all || (a.p.mask.window > 0 && kblk * kDkdvKeys < a.p.mask.sinks))
     dkdv_block<DT, true, ROPE>(a, wg);
   else
     dkdv_block<DT, false, ROPE>(a, wg);

@@ -146,6 +146,10 @@ struct FwdParams {
   int hpw;           // heads per workgroup (a divisor of H/G): waves 0..hpw-1 share rows
   int qpw;           // 64-row query tiles per workgroup (4 / hpw)
   int n_qblk;        // workgroup row blocks per head = ceil(S / (64 * qpw))
+  int xcd_hg;        // > 0: head groups per XCD (workgroup order that keeps kv heads on one
+                     // XCD, see fwd_block_order); 0: plain q-block-major order
+  int xcd_kv;        // with xcd_hg: > 0 = head groups per kv head, an XCD finishing one kv
+                     // head before the next; 0 = its kv heads' row blocks interleaved
   void* q_rot;       // with rope.enabled: optional output of the rotated Q (element type)
   RopeSpec rope;     // query i sits at position i
 };
@@ -182,6 +186,8 @@ struct BwdParams {
   MaskSpec mask;
   int hpw, qpw, n_qblk;  // dQ pass: same row decomposition as the forward
   int n_kblk;            // dK/dV pass: kDkdvKeys-key blocks per kv head
+  int precise_all;       // dK/dV pass: every block takes P and dS as rounded value plus
+                         // rounded residual (short sequences and short windows, where P is large)
 };
 
 // The only argument of the dK/dV, dQ and one-launch backward kernels: the parameters and
