@@ -33,6 +33,11 @@ namespace gqa {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+// Lazy maximum (see decode_tile): a tile is redone against its own maximum when a lane's
+// partial row sum exceeds this, and the running maximum is raised when the tile's exceeds
+// it by more than kDecodeRescale (log2 units).
+constexpr float kDecodeSumGuard = 65536.0f;
+constexpr float kDecodeRescale = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -102,35 +107,50 @@ __device__ __forceinline__ void decode_tile(const char* kt, const char* vt, int 
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
-    mx = max_across_halves(mx) * c2;
-    const float mnew = vmax(m[cb], mx);
-    // a row with no visible key yet keeps maximum -inf: no rescale, and P = exp2(-inf) = 0
-    const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(m[cb] - mnew);
-    const float nm = mnew == -INFINITY ? 0.f : -mnew;
+    // Lazy maximum, as in the prefill forward: the tile is exponentiated against the running
+    // maximum m, which only keeps exp2 in range.  When a lane's partial row sum leaves
+    // (0, kSumGuard] (some P > 2^16 / 64, an overflow) or a row inside the sequence has no
+    // maximum yet, the tile takes the exact path: its maximum, the running maximum raised
+    // when it grew by more than 2^8 (with O and the sum rescaled), and exponentiated again.
     u32x4 pf[2][2];  // P^T as B operands [half][step t]
     float ls = 0.f;
+    auto exponentiate = [&](float nm) __attribute__((always_inline)) {
+      ls = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float pv[8];
+        for (int t = 0; t < 2; ++t) {
+          float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[kb][8 * t + e], c2, nm));
+          for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[kb][8 * t + e], c2, nm));
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pf[kb][t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
-          ls += pv[2 * w] + pv[2 * w + 1];
+          for (int w = 0; w < 4; ++w) {
+            pf[kb][t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
+            ls += pv[2 * w] + pv[2 * w + 1];
+          }
         }
-      }
-    l[cb] = l[cb] * alpha + ls;
-    m[cb] = mnew;
+    };
+    exponentiate(m[cb] == -INFINITY ? 0.f : -m[cb]);
+    const bool need = !(ls <= kDecodeSumGuard) | ((m[cb] == -INFINITY) & (pos[cb] >= 0));
+    if (__builtin_expect(wave_any(need), 0)) {
+      float mx = s[0][0];
 #pragma unroll
-    for (int db = 0; db < 2; ++db) o[cb][db] *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
+      mx = max_across_halves(mx) * c2;
+      // raise the maximum when it grew by more than 2^8 (or the row had none)
+      const float mnew = (mx > m[cb] + kDecodeRescale) ? mx : m[cb];
+      // a row with no visible key yet keeps maximum -inf: no rescale, and P = exp2(-inf) = 0
+      const float alpha = mnew == -INFINITY || m[cb] == -INFINITY ? 1.f : exp2_fast(m[cb] - mnew);
+      asm volatile("" ::: "memory");  // keep the rescale inside this rare branch
+      l[cb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[cb][db] *= alpha;
+      m[cb] = mnew;
+      exponentiate(mnew == -INFINITY ? 0.f : -mnew);
+    }
+    l[cb] += ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
