@@ -123,7 +123,7 @@ def load_traffic(kernel, wname, path=None):
 KERNEL_KEYS = {"rope_kernel": "rope", "fwd_fp8_kernel": "fwd_fp8", "vt_permute_kernel": "vt_permute",
                "fwd_mfma_kernel": "fwd", "bwd_preprocess_kernel": "bwd_preprocess",
                "bwd_fused_kernel": "bwd_grads", "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq",
-               "decode_split_kernel": "decode", "decode_merge_kernel": "decode_merge", "copyBuffer": "copy"}
+               "decode_split_kernel": "decode", "decode_shared_kernel": "decode", "decode_merge_kernel": "decode_merge", "copyBuffer": "copy"}
 COPY_BYTES = 1 << 30
 
 

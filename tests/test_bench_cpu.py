@@ -51,16 +51,23 @@ def test_counter_reduction_calibrates_on_the_large_copy(tmp_path):
     assert bench.load_traffic("fwd", "other", path=str(out)) is None
 
 
-def test_committed_traffic_reads_back():
-    # every bench line reads the committed summary: it must parse and hold the default
-    # step's dominant kernel.  After a kernel change its digest is stale until counters are
-    # taken again on a GPU, and the bench then reports traffic as null.
+def test_committed_counters_read_back():
+    # every bench line reads the committed summaries: they must parse and hold the default
+    # line's kernels.  After a kernel change their digest is stale until counters are taken
+    # again on a GPU, and the bench then reports traffic, hbm_gbs and mfma_busy as null.
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         rec = json.load(f)
-    assert "bwd_grads@step" in rec["kernels"] and rec["calibration"]
-    if rec["source_digest"] != bench.source_digest():
+    with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+        ctr = json.load(f)
+    # the default line's kernels: the windowed forward (its roofline), the causal forward and
+    # the backward's kernels
+    for key in ("fwd@c4", "fwd@c3", "bwd_dkdv@c5", "bwd_dq@c5", "bwd_preprocess@c5"):
+        assert key in rec["kernels"] and key in ctr["kernels"], key
+    assert rec["calibration"]
+    if rec["source_digest"] != bench.source_digest() or ctr["source_digest"] != bench.source_digest():
         pytest.skip("counters predate the current kernel sources")
-    assert bench.load_traffic("bwd_grads", "step") == rec["kernels"]["bwd_grads@step"]["bytes_per_launch"]
+    assert bench.load_traffic("fwd", "c4") == rec["kernels"]["fwd@c4"]["bytes_per_launch"]
+    assert 0 < bench.load_counters("fwd", "c4")["mfma_busy"] < 1
 
 
 SQ_FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
