@@ -782,6 +782,9 @@ def main():
     if args.warmup is None:
         args.warmup = 1 if long_step else 5
     if args.workload == "headline":
+        if args.rope or args.fp8:
+            print("--rope and --fp8 apply to a single workload (--workload c3, c4, c5, step)", file=sys.stderr)
+            sys.exit(2)
         import torch
 
         import transformer_attention_07_amd as gqa
