@@ -45,7 +45,8 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kSumGuard = 65536.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// Per-wave state and the pieces of one key tile, processed as two 32-key halves.
+// Per-wave state and the pieces of one key tile.  The loop works in units of one 32-key
+// half and one 32-row column block (a 32 x 32 block of scores).
 template <int DT>
 struct FwdWave {
   int lane, l32, hl;
@@ -56,11 +57,9 @@ struct FwdWave {
   f32x16 o[2][2];   // O^T accumulators [d block][column block]
   float mrow[2];    // running maximum (log2 units) per column block
   float lrow[2];    // running sum (this lane's half of the keys)
-  float alpha[2];   // rescale factor decided by the last softmax
   float nmuse[2];   // -mrow, or 0 while the row has seen no visible key (mrow = -inf)
   int lim_hi;       // a key half [k, k + 31] is fully visible to all 64 rows iff
   int win_lo;       //   k + 31 <= lim_hi && (k >= win_lo || k + 31 < m.sinks)
-  bool rescale;     // wave-uniform: the last softmax raised the maximum
   int koff[4];      // lane's byte offset of the K operand, contraction step ks (block 0)
   int voff[2][2];   // lane's byte offset of the transposed V read [d block][second row group]
 
@@ -82,14 +81,12 @@ struct FwdWave {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = *(const u32x4*)(kl + kb * 4096 + koff[ks]);
   }
-  // S^T[cb] = K Q^T[cb] from loaded K operands
-  __device__ __forceinline__ void scores(const u32x4 (&a)[4], f32x16 (&s)[2]) const {
+  // S^T of column block CB: K Q^T[CB] from loaded K operands
+  template <int CB>
+  __device__ __forceinline__ void scores(const u32x4 (&a)[4], f32x16& s) const {
+    s = mfma32<DT>(a[0], qf[CB][0], f32x16{});
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32<DT>(a[0], qf[cb][0], f32x16{});
-#pragma unroll
-    for (int ks = 1; ks < 4; ++ks)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32<DT>(a[ks], qf[cb][ks], s[cb]);
+    for (int ks = 1; ks < 4; ++ks) s = mfma32<DT>(a[ks], qf[CB][ks], s);
   }
 
   // V^T operands of key half kb of the tile in `vl` (row-major tile read transposed: rows
@@ -109,14 +106,13 @@ struct FwdWave {
         a[db][t] = u32x4{ux[0], ux[1], uy[0], uy[1]};
       }
   }
-  // O^T[db][cb] += V^T[db] P^T[cb] from loaded V operands
-  __device__ __forceinline__ void accumulate(const u32x4 (&a)[2][2], const u32x4 (&pf)[2][2]) {
+  // O^T[db][CB] += V^T[db] P^T[CB] from loaded V operands
+  template <int CB>
+  __device__ __forceinline__ void accumulate(const u32x4 (&a)[2][2], const u32x4 (&pf)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) o[db][cb] = mfma32<DT>(a[db][t], pf[cb][t], o[db][cb]);
+      for (int db = 0; db < 2; ++db) o[db][CB] = mfma32<DT>(a[db][t], pf[t], o[db][CB]);
   }
 
   // wave-uniform (a scalar branch): bitwise tests, then readfirstlane
@@ -124,106 +120,87 @@ struct FwdWave {
     return __builtin_amdgcn_readfirstlane((int)(k + 31 <= lim_hi) & ((int)(k >= win_lo) | (int)(k + 31 < m.sinks))) != 0;
   }
 
-  // hide keys that are not visible (halves that are not fully visible only).  Register r of
-  // this lane holds key k0 + 4*hl + rr(r) with rr(r) = 8*(r/4) + r%4 a compile-time constant,
-  // so every test is one compare of rr against a per-lane bound.
-  __device__ __forceinline__ void mask(f32x16 (&s)[2], int k0) const {
+  // hide the keys of half [k0, k0 + 31] that column block CB's rows do not see.  Register r
+  // of this lane holds key k0 + 4*hl + rr(r) with rr(r) = 8*(r/4) + r%4 a compile-time
+  // constant, so every test is one compare of rr against a per-lane bound.
+  template <int CB>
+  __device__ __forceinline__ void mask(f32x16& s, int k0) const {
     const int base = k0 + 4 * hl;
     const int kmax = m.S - 1 - base;  // rr <= kmax: key inside the sequence
+    const int i = q0 + CB * 32 + l32;
+    const int causal_hi = m.causal ? i - base : kmax;       // rr <= causal_hi: not in the future
+    const int hi = causal_hi < kmax ? causal_hi : kmax;
+    const int wlo = m.window > 0 ? i - m.window + 1 - base : -(1 << 30);  // rr >= wlo: in window
+    const int sink_hi = m.sinks - 1 - base;                  // rr <= sink_hi: a sink
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int i = q0 + cb * 32 + l32;
-      const int causal_hi = m.causal ? i - base : kmax;       // rr <= causal_hi: not in the future
-      const int hi = causal_hi < kmax ? causal_hi : kmax;
-      const int win_lo = m.window > 0 ? i - m.window + 1 - base : -(1 << 30);  // rr >= win_lo: in window
-      const int sink_hi = m.sinks - 1 - base;                  // rr <= sink_hi: a sink
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 8 * (r >> 2) + (r & 3);
-        const bool ok = (rr <= hi) && (rr >= win_lo || rr <= sink_hi);
-        s[cb][r] = ok ? s[cb][r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 8 * (r >> 2) + (r & 3);
+      const bool ok = (rr <= hi) && (rr >= wlo || rr <= sink_hi);
+      s[r] = ok ? s[r] : -INFINITY;
     }
   }
 
-  // running-maximum update for one 32-key half (already masked): sets rescale and, when the
-  // maximum is raised, alpha/mrow/lrow (rare)
-  __device__ __forceinline__ void decide(const f32x16 (&s)[2]) {
-    float mx[2];
-    bool need = false;
+  // Running-maximum update of column block CB from one (masked) unit of scores: when some
+  // row's maximum grew by more than the threshold, every row takes its new maximum and O
+  // and the sums of the block are rescaled (rare).
+  template <int CB>
+  __device__ __forceinline__ void decide(const f32x16& s) {
+    float a = vmax(s[0], s[1]);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float a = vmax(s[cb][0], s[cb][1]);
+    for (int r = 2; r < 16; r += 2) a = vmax(vmax(a, s[r]), s[r + 1]);
+    uint32_t u = __builtin_bit_cast(uint32_t, a);
+    auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float mx = vmax(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1])) * c2;
+    if (__builtin_expect(wave_any(mx > mrow[CB] + kRescaleThreshold), 0)) {
+      const float mnew = vmax(mrow[CB], mx);
+      const float alpha = mnew != -INFINITY ? exp2_fast(mrow[CB] - mnew) : 1.0f;
+      mrow[CB] = mnew;
+      nmuse[CB] = mnew == -INFINITY ? 0.f : -mnew;
+      lrow[CB] *= alpha;
+      // keep this block a real branch: O *= 1 is an identity, and hoisting the multiplies
+      // out of the (rare) branch would put them on every step
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) a = vmax(vmax(a, s[cb][r]), s[cb][r + 1]);
-      uint32_t u = __builtin_bit_cast(uint32_t, a);
-      auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      mx[cb] = vmax(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1])) * c2;
-      need = need | (mx[cb] > mrow[cb] + kRescaleThreshold);
-    }
-    rescale = wave_any(need);
-    if (__builtin_expect(rescale, 0)) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const float mnew = vmax(mrow[cb], mx[cb]);
-        alpha[cb] = mnew != -INFINITY ? exp2_fast(mrow[cb] - mnew) : 1.0f;
-        mrow[cb] = mnew;
-        nmuse[cb] = mnew == -INFINITY ? 0.f : -mnew;
-        lrow[cb] *= alpha[cb];
-      }
-      apply_rescale();
+      for (int db = 0; db < 2; ++db) o[db][CB] *= alpha;
     }
   }
 
-  // P^T of one half tile at the current maximum, packed into B operands [cb][t]
-  __device__ __forceinline__ void probs(const f32x16 (&s)[2], u32x4 (&pf)[2][2], float (&ls)[2]) {
+  // P^T of one unit at the current maximum, packed into B operands [t]
+  template <int CB>
+  __device__ __forceinline__ void probs(const f32x16& s, u32x4 (&pf)[2], float& ls) const {
+    float lsum = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float lsum = 0.f;
+    for (int t = 0; t < 2; ++t) {
+      float pv[8];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float pv[8];
+      for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[8 * t + e], c2, nmuse[CB]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[cb][8 * t + e], c2, nmuse[cb]));
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pf[cb][t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
-          lsum += pv[2 * w] + pv[2 * w + 1];
-        }
+      for (int w = 0; w < 4; ++w) {
+        pf[t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
+        lsum += pv[2 * w] + pv[2 * w + 1];
       }
-      ls[cb] = lsum;
     }
+    ls = lsum;
   }
 
-  // Softmax of one (masked) half against the running maximum.  The maximum only serves to
+  // Softmax of one (masked) unit against the running maximum.  The maximum only serves to
   // keep exp2 in range, so it is left alone unless a lane's partial row sum shows an
   // exponent above log2(kSumGuard / 16) or the row has no maximum yet (no visible key so
-  // far); then the half's maximum is taken (decide, which raises it and rescales O and the
-  // row sums) and the half is exponentiated again.  P therefore stays below 2^16: the
+  // far); then the unit's maximum is taken (decide, which raises it and rescales O and the
+  // row sums) and the unit is exponentiated again.  P therefore stays below 2^16: the
   // rounded operands and fp32 sums keep their relative precision at any magnitude.  (Rows
   // past the end of the sequence may never see a key; they do not hold the slow path.)
-  __device__ __forceinline__ void softmax_half(const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
-    float ls[2];
-    probs(s, pf, ls);
+  template <int CB>
+  __device__ __forceinline__ void softmax(const f32x16& s, u32x4 (&pf)[2]) {
+    float ls;
+    probs<CB>(s, pf, ls);
     // bitwise combination: one ballot, no per-lane branches
-    const bool need = !(ls[0] <= kSumGuard) | !(ls[1] <= kSumGuard) | ((mrow[0] == -INFINITY) & (q0 + l32 < m.S)) |
-                      ((mrow[1] == -INFINITY) & (q0 + 32 + l32 < m.S));
+    const bool need = !(ls <= kSumGuard) | ((mrow[CB] == -INFINITY) & (q0 + CB * 32 + l32 < m.S));
     if (__builtin_expect(wave_any(need), 0)) {
-      decide(s);
-      probs(s, pf, ls);
+      decide<CB>(s);
+      probs<CB>(s, pf, ls);
     }
-    lrow[0] += ls[0];
-    lrow[1] += ls[1];
-  }
-
-  __device__ __forceinline__ void apply_rescale() {
-    // keep this block a real branch: O *= 1 is an identity, and hoisting the 64 multiplies
-    // out of the (rare) branch would put them on every step
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) o[db][cb] *= alpha[cb];
+    lrow[CB] += ls;
   }
 };
 
@@ -356,53 +333,76 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     for (int cb = 0; cb < 2; ++cb) W.o[db][cb] = f32x16{};
   W.mrow[0] = W.mrow[1] = -INFINITY;
   W.lrow[0] = W.lrow[1] = 0.f;
-  W.alpha[0] = W.alpha[1] = 1.f;
   W.nmuse[0] = W.nmuse[1] = 0.f;
   W.lim_hi = __builtin_amdgcn_readfirstlane(W.m.causal ? imin(W.q0, S - 1) : S - 1);
   W.win_lo = __builtin_amdgcn_readfirstlane(W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30));
-  W.rescale = false;
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // Half-tile software pipeline.  A step softmaxes one 32-key half while the matrix cores
-  // compute the scores of the following half, then adds that half's P V; so tile n reads
-  // K_n and K_{n+1} and V_n.  K and V tiles are triple-buffered (buffer n % 3) and the loop
-  // is unrolled by three, so every buffer is fixed at compile time.  One barrier per tile:
-  // right after it, the direct loads of K_{n+2} and V_{n+1} go into the buffers of K_{n-1}
-  // and V_{n-2}, which no wave reads any more; they have the whole tile to land and the
-  // next barrier drains them, so nothing is in flight across the loop's back edge.  Loads
-  // past the last tile read zeros (no traffic), which keeps the steps unconditional.
-  f32x16 sc[2], sn[2];  // S^T of the half being softmaxed / the next half, [column block]
-  u32x4 ka[4];           // K operands of the next scores, read one step ahead
-  u32x4 va[2][2];        // V^T operands of this step's P V, read before its softmax
-  W.load_k(k_lds0, 0, ka);
-  W.scores(ka, sc);
-  W.load_k(k_lds0, 1, ka);
+  // Software pipeline over units (one 32-key half, one 32-row column block): a unit's
+  // softmax runs while the matrix cores compute the previous unit's P V and the next
+  // unit's scores, all three independent of one another.  Between two softmax ends
+  // (where the rare rescale branch sits) nothing else breaks the code, so the compiler
+  // interleaves the softmax's vector instructions with those eight MFMAs inside the wave.
+  // Tile n's units are (half 0, block 0), (0, 1), (1, 0), (1, 1); operands are read from
+  // LDS a unit or two ahead, into two sets of registers per operand: K half 0 / half 1 and
+  // V half 0 / half 1, scores and P alternating between two sets.  Tile n reads K_n,
+  // K_{n+1} (the next tile's first scores) and V_n.  K and V tiles are triple-buffered
+  // (buffer n % 3) and the loop is unrolled by three, so every buffer is fixed at compile
+  // time.  One barrier per tile: right after it, the direct loads of K_{n+2} and V_{n+1}
+  // go into the buffers of K_{n-1} and V_{n-2}, which no wave reads any more; they have
+  // the whole tile to land and the next barrier drains them, so nothing is in flight
+  // across the loop's back edge.  Loads past the last tile read zeros (no traffic), which
+  // keeps the steps unconditional.  The (rare) mask of a unit that is not fully visible
+  // sits at the unit's start, ahead of its matrix products, so it splits nothing.
+  f32x16 sx, sy;               // S^T of the units softmaxed at block 0 / block 1
+  u32x4 ka0[4], ka1[4];        // K operands of key half 0 / half 1
+  u32x4 va0[2][2], va1[2][2];  // V^T operands of key half 0 / half 1
+  u32x4 px[2], py[2];          // P^T of the units softmaxed from sx / sy
+  W.load_k(k_lds0, 0, ka0);
+  W.template scores<0>(ka0, sx);
+  // the first unit's P V (of no earlier unit) adds zero
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    py[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < 2; ++db) va1[db][t] = u32x4{0u, 0u, 0u, 0u};
+  }
 
   auto tile = [&](auto par, int n) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
+    char* kn = P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2;    // K_n
     char* kn1 = P == 0 ? k_lds1 : P == 1 ? k_lds2 : k_lds0;   // K_{n+1}
     char* kn2 = P == 0 ? k_lds2 : P == 1 ? k_lds0 : k_lds1;   // receives K_{n+2}
     char* vn = P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2;    // V_n
     char* vn1 = P == 0 ? v_lds1 : P == 1 ? v_lds2 : v_lds0;   // receives V_{n+1}
     const int k0 = tr.tile(n) * kTile;
-    u32x4 pf[2][2];
     stage_rows(krs, kn2, tile_row(n + 2), voff, wave);
     stage_rows(vrs, vn1, tile_row(n + 1), voff, wave);
-    // half 0: scores of (n, 1) (operands from the previous step) while exponentiating (n, 0)
-    W.scores(ka, sn);
-    W.load_v(vn, 0, va);
-    W.load_k(kn1, 0, ka);
-    if (__builtin_expect(!W.half_full(k0), 0)) W.mask(sc, k0);
-    W.softmax_half(sc, pf);
-    W.accumulate(va, pf);
-    // half 1: scores of (n + 1, 0) while exponentiating (n, 1)
-    W.scores(ka, sc);
-    W.load_v(vn, 1, va);
-    W.load_k(kn1, 1, ka);
-    if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.mask(sn, k0 + 32);
-    W.softmax_half(sn, pf);
-    W.accumulate(va, pf);
+    // (half 0, block 0) from sx; P V of (n - 1, half 1, block 1); scores of (half 0, block 1)
+    if (__builtin_expect(!W.half_full(k0), 0)) W.template mask<0>(sx, k0);
+    W.template accumulate<1>(va1, py);
+    W.template scores<1>(ka0, sy);
+    W.load_k(kn, 1, ka1);
+    W.load_v(vn, 0, va0);
+    W.template softmax<0>(sx, px);
+    // (half 0, block 1) from sy; P V of (half 0, block 0); scores of (half 1, block 0)
+    if (__builtin_expect(!W.half_full(k0), 0)) W.template mask<1>(sy, k0);
+    W.template accumulate<0>(va0, px);
+    W.template scores<0>(ka1, sx);
+    W.template softmax<1>(sy, py);
+    // (half 1, block 0) from sx; P V of (half 0, block 1); scores of (half 1, block 1)
+    if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.template mask<0>(sx, k0 + 32);
+    W.template accumulate<1>(va0, py);
+    W.template scores<1>(ka1, sy);
+    W.load_k(kn1, 0, ka0);
+    W.load_v(vn, 1, va1);
+    W.template softmax<0>(sx, px);
+    // (half 1, block 1) from sy; P V of (half 1, block 0); scores of (n + 1, half 0, block 0)
+    if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.template mask<1>(sy, k0 + 32);
+    W.template accumulate<0>(va1, px);
+    W.template scores<0>(ka0, sx);
+    W.template softmax<1>(sy, py);
     lds_barrier<0>();  // this tile's loads have landed; its buffers are read no more
   };
   for (int n = 0; n < nt; n += 3) {
@@ -412,6 +412,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     if (n + 2 >= nt) break;
     tile(std::integral_constant<int, 2>{}, n + 2);
   }
+  W.template accumulate<1>(va1, py);  // P V of the last unit
 
   if constexpr (ROPE) {
     // the rotated Q tile for the backward, stored once the tile loop is done so that these
