@@ -26,6 +26,8 @@
 // O^T += V^T P^T from registers, and V^T comes from the row-major V tile through
 // ds_read_b64_tr_b16.  The K and V operands of a tile are read once and shared by the
 // (up to four) 32-row blocks.
+#include <type_traits>
+
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -40,7 +42,9 @@ constexpr float kDecodeSumGuard = 65536.0f;
 constexpr float kDecodeRescale = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // Direct-to-LDS staging of a 64-row tile by one wave: instruction j (0..7) writes lane i's
 // 16 bytes to LDS bytes 1024 j + 16 i (rows 8j .. 8j+7), so the lane fetches the global
@@ -62,7 +66,7 @@ __device__ __forceinline__ void wait_counts() {
 // rows held as B operands: S^T = K Q^T, the online-softmax update (exact maximum, rescale of
 // O and of the row sum), O^T += V^T P^T.  `full`: every pair of the tile is visible, no mask.
 template <int DT, int NB>
-__device__ __forceinline__ void decode_tile(const char* kt, const char* vt, int k0, bool full,
+__device__ __forceinline__ void decode_tile(const lds_char* kt, const lds_char* vt, int k0, bool full,
                                             const u32x4 (&qf)[NB][4], const int (&pos)[NB],
                                             f32x16 (&o)[NB][2], float (&m)[NB], float (&l)[NB],
                                             const int (&koff)[4], const int (&voff)[2][2], int hl, float c2,
@@ -72,18 +76,16 @@ __device__ __forceinline__ void decode_tile(const char* kt, const char* vt, int 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = *(const u32x4*)(kt + kb * 4096 + koff[ks]);
+    for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = *(const lds_u32x4*)(kt + kb * 4096 + koff[ks]);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const char* base = vt + (kb * 32 + 16 * t) * 128;
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + voff[db][0]));
-        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(__attribute__((address_space(3))) char*)(base + voff[db][1]));
+        const lds_char* base = vt + (kb * 32 + 16 * t) * 128;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[db][0]));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[db][1]));
         const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
         va[kb][db][t] = u32x4{ux[0], ux[1], uy[0], uy[1]};
       }
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
     return i < my_nt ? p.tiles.tile(part + i * n_part) * kTile : Skv;
   };
   // 16 direct loads: the K tile, then the V tile
-  auto stage = [&](char* kt, char* vt, int row0) __attribute__((always_inline)) {
+  auto stage = [&](lds_char* kt, lds_char* vt, int row0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + 1024 * j), 16, row0 * 128 + soff[j], 0, 0, 0);
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
     l[cb] = 0.f;
   }
 
-  auto compute = [&](const char* kt, const char* vt, int i) __attribute__((always_inline)) {
+  auto compute = [&](const lds_char* kt, const lds_char* vt, int i) __attribute__((always_inline)) {
     const int k0 = p.tiles.tile(part + i * n_part) * kTile;
     // every row of the chunk sees every key of the tile: rows at Skv - Sq .. Skv - 1
     const bool full = __builtin_amdgcn_readfirstlane(
@@ -264,13 +266,17 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
   // fixed at compile time: the next tile's 16 loads go into the other buffers, the wait
   // leaves exactly those in flight, and the LDS reads of the current buffers are waited
   // for before the next iteration's loads overwrite them.
-  stage(k_st0[wave], v_st0[wave], tile_row(0));
+  lds_char* const k0b = (lds_char*)k_st0[wave];
+  lds_char* const k1b = (lds_char*)k_st1[wave];
+  lds_char* const v0b = (lds_char*)v_st0[wave];
+  lds_char* const v1b = (lds_char*)v_st1[wave];
+  stage(k0b, v0b, tile_row(0));
   auto body = [&](auto par, int i) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    stage(P ? k_st0[wave] : k_st1[wave], P ? v_st0[wave] : v_st1[wave], tile_row(i + 1));
+    stage(P ? k0b : k1b, P ? v0b : v1b, tile_row(i + 1));
     wait_counts<16, 15>();
     asm volatile("" ::: "memory");
-    compute(P ? k_st1[wave] : k_st0[wave], P ? v_st1[wave] : v_st0[wave], i);
+    compute(P ? k1b : k0b, P ? v1b : v0b, i);
     asm volatile("" ::: "memory");
     wait_counts<63, 0>();
   };
@@ -313,16 +319,45 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
 // (each issues the direct loads j with j % NRB == wave), one barrier per tile.
 constexpr int kSharedStages = 4;
 
+// The ring's buffers, each a distinct LDS object selected at compile time, so that every
+// LDS address is a known constant (typed LDS pointers from here on: no generic pointer is
+// ever cast back to LDS).
+__shared__ __attribute__((aligned(1024))) char g_dec_k0[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_k1[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_k2[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_k3[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_v0[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_v1[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_v2[8192];
+__shared__ __attribute__((aligned(1024))) char g_dec_v3[8192];
+// f(integral_constant<int, U>) for U = B .. E - 1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+template <int U>
+__device__ __forceinline__ lds_char* ring_k() {
+  static_assert(U >= 0 && U < kSharedStages, "ring slot");
+  if constexpr (U == 0) return (lds_char*)g_dec_k0;
+  else if constexpr (U == 1) return (lds_char*)g_dec_k1;
+  else if constexpr (U == 2) return (lds_char*)g_dec_k2;
+  else return (lds_char*)g_dec_k3;
+}
+template <int U>
+__device__ __forceinline__ lds_char* ring_v() {
+  static_assert(U >= 0 && U < kSharedStages, "ring slot");
+  if constexpr (U == 0) return (lds_char*)g_dec_v0;
+  else if constexpr (U == 1) return (lds_char*)g_dec_v1;
+  else if constexpr (U == 2) return (lds_char*)g_dec_v2;
+  else return (lds_char*)g_dec_v3;
+}
+
 template <int DT, int NRB>
 __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char k_sh0[8192];
-  __shared__ __attribute__((aligned(1024))) char k_sh1[8192];
-  __shared__ __attribute__((aligned(1024))) char k_sh2[8192];
-  __shared__ __attribute__((aligned(1024))) char k_sh3[8192];
-  __shared__ __attribute__((aligned(1024))) char v_sh0[8192];
-  __shared__ __attribute__((aligned(1024))) char v_sh1[8192];
-  __shared__ __attribute__((aligned(1024))) char v_sh2[8192];
-  __shared__ __attribute__((aligned(1024))) char v_sh3[8192];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = row block
@@ -378,7 +413,7 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
     return i < my_nt ? p.tiles.tile(part + i * n_part) * kTile : Skv;
   };
   // this wave's share of the tile's 16 direct loads (8 K, 8 V)
-  auto stage = [&](char* kt, char* vt, int row0) __attribute__((always_inline)) {
+  auto stage = [&](lds_char* kt, lds_char* vt, int row0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (j % NRB == wave) {
@@ -389,8 +424,9 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
                                                    row0 * 128 + soff[j - 8], 0, 0, 0);
       }
   };
-  // loads per tile of the wave with the fewest: waiting until at most twice that many are
-  // outstanding guarantees that this wave's loads of the oldest staged tile have landed
+  // loads per tile of the wave with the fewest: with kSharedStages - 1 tiles in flight,
+  // waiting until at most kSharedStages - 2 tiles' worth are outstanding guarantees that
+  // this wave's loads of the oldest staged tile have landed
   constexpr int kMinPerTile = 16 / NRB;
 
   f32x16 o[1][2];
@@ -399,26 +435,26 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
   m[0] = -INFINITY;
   l[0] = 0.f;
 
-  char* kb[kSharedStages] = {k_sh0, k_sh1, k_sh2, k_sh3};
-  char* vb[kSharedStages] = {v_sh0, v_sh1, v_sh2, v_sh3};
-#pragma unroll
-  for (int u = 0; u < kSharedStages - 1; ++u) stage(kb[u], vb[u], tile_row(u));
+  static_for<0, kSharedStages - 1>([&](auto u) __attribute__((always_inline)) {
+    constexpr int U = decltype(u)::value;
+    stage(ring_k<U>(), ring_v<U>(), tile_row(U));
+  });
   // Tile i: wait for this wave's loads of tile i, barrier (every wave's loads of tile i have
-  // landed and every wave is done with tile i - 1), load tile i + 3 into tile i - 1's buffer,
-  // compute tile i.
+  // landed and every wave is done with tile i - 1), load tile i + kSharedStages - 1 into
+  // tile i - 1's buffer, compute tile i.
   auto body = [&](auto par, int i) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     constexpr int F = (P + kSharedStages - 1) % kSharedStages;
     asm volatile("" ::: "memory");
-    wait_counts<2 * kMinPerTile, 0>();
+    wait_counts<(kSharedStages - 2) * kMinPerTile, 0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    stage(kb[F], vb[F], tile_row(i + kSharedStages - 1));
+    stage(ring_k<F>(), ring_v<F>(), tile_row(i + kSharedStages - 1));
     const int k0 = tile_row(i);
     const bool full = __builtin_amdgcn_readfirstlane(
                           (int)rows_full & (int)(k0 + 63 <= Skv - Sq) &
                           ((int)(W == 0) | (int)(k0 > Skv - 1 - W) | (int)(k0 + 63 < NS))) != 0;
-    decode_tile<DT, 1>(kb[P], vb[P], k0, full, qf, pos, o, m, l, koff, voff, hl, c2, Skv, W, NS);
+    decode_tile<DT, 1>(ring_k<P>(), ring_v<P>(), k0, full, qf, pos, o, m, l, koff, voff, hl, c2, Skv, W, NS);
   };
   for (int i = 0; i < my_nt; i += kSharedStages) {
     body(std::integral_constant<int, 0>{}, i);
@@ -453,7 +489,10 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
 }
 
 // One wave per output row (b, h, t): lane = d.  O = sum_p w_p O_p / sum_p w_p l_p with
-// w_p = 2^(m_p - max_p m_p); lse = (max_p m_p + log2 sum_p w_p l_p) ln 2.
+// w_p = 2^(m_p - max_p m_p); lse = (max_p m_p + log2 sum_p w_p l_p) ln 2.  Lane j holds
+// the maximum and sum of partial c + j of a chunk of 64 partials; the weights reach every
+// lane through readlane, and each step issues the loads of 16 partials' O before their
+// multiply-adds, so the loads are in flight together.
 template <int DT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -468,18 +507,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int n_part = p.n_part;
   const float* ml = p.part_ml + (size_t)set * n_part * 2 * kDecodeRows + rr;
   const float* po = p.part_o + ((size_t)set * n_part * kDecodeRows + rr) * kHeadDim + lane;
-  // unrolled so that the partials' loads are in flight together
+  auto part_m = [&](int i) __attribute__((always_inline)) {
+    return i < n_part ? ml[(size_t)i * 2 * kDecodeRows] : -INFINITY;
+  };
   float mstar = -INFINITY;
-#pragma unroll 8
-  for (int i = 0; i < n_part; ++i) mstar = vmax(mstar, ml[(size_t)i * 2 * kDecodeRows]);
+  for (int c = 0; c < n_part; c += 64) mstar = vmax(mstar, part_m(c + lane));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) mstar = vmax(mstar, __shfl_xor(mstar, s, 64));
   float L = 0.f, acc = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < n_part; ++i) {
-    const float mi = ml[(size_t)i * 2 * kDecodeRows];
+  for (int c = 0; c < n_part; c += 64) {
+    const int i = c + lane;
+    const float mi = part_m(i);
     const float w = mi == -INFINITY ? 0.f : exp2_fast(mi - mstar);
-    L += w * ml[(size_t)i * 2 * kDecodeRows + kDecodeRows];
-    acc += w * po[(size_t)i * kDecodeRows * kHeadDim];
+    L += i < n_part ? w * ml[(size_t)i * 2 * kDecodeRows + kDecodeRows] : 0.f;
+    const int cnt = imin(64, n_part - c);
+    const int wbits = __builtin_bit_cast(int, w);
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+      float ov[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) ov[u] = j0 + u < cnt ? po[(size_t)(c + j0 + u) * kDecodeRows * kHeadDim] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, j0 + u)) * ov[u];
+    }
   }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) L += __shfl_xor(L, s, 64);
   const float out = acc / L;
   ((uint16_t*)p.o)[row * kHeadDim + lane] = (uint16_t)(pack2<DT>(out, 0.f) & 0xFFFFu);
   if (lane == 0) p.lse[row] = (mstar + log2f(L)) * kLn2;
