@@ -141,3 +141,14 @@ def test_row_decomposition_labels():
     assert bench.row_decomposition(WORKLOADS["c3"])["fwd"] == 256 * 32
     c5 = bench.row_decomposition(WORKLOADS["c5"])
     assert c5["fwd"] == 64 * 4 * 8 and c5["bwd_dkdv"] == 32 * 4 * 8
+
+
+@pytest.mark.parametrize("flag", ["--rope", "--fp8"])
+def test_default_line_rejects_single_workload_flags(flag):
+    # --rope / --fp8 change one workload's kernels; the default line times several, so the
+    # combination is refused before anything touches a GPU
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), flag],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--workload" in r.stderr

@@ -24,7 +24,7 @@ CASES = [
     (["--workload", "c3"], False),
     (["--workload", "decode16"], False),
     (["--workload", "rope_k"], False),
-    (["--rope"], False),
+    (["--rope", "--workload", "step"], False),
     (["--fp8", "--workload", "c2"], False),
 ]
 
@@ -51,9 +51,11 @@ def test_bench_line(args, cpu):
     assert rf["bound"] in ("mfma", "hbm") and rf["achieved"] > 0 and 0 < rf["frac"] < 1
     if not args:  # the default line: the windowed forward at S=65536, with the other headline kernels
         assert d["config"]["S"] == 65536 and d["config"]["window"] == 16384 and d["config"]["num_sinks"] == 2048
-        for k in ("fwd@c4", "fwd@c3", "bwd_preprocess@c5", "bwd_dkdv@c5", "bwd_dq@c5", "bwd@c5"):
+        for k in ("fwd@c4", "fwd@c3", "bwd_preprocess@c5", "bwd_dkdv@c5", "bwd_dq@c5", "bwd_grads@c5", "bwd@c5"):
             assert d["kernels"][k]["ms"] > 0, k
-        for k in ("fwd@c4", "fwd@c3", "bwd_dkdv@c5", "bwd_dq@c5"):
+        kc5 = d["kernels"]
+        assert abs(kc5["bwd@c5"]["ms"] - kc5["bwd_preprocess@c5"]["ms"] - kc5["bwd_grads@c5"]["ms"]) < 1e-3
+        for k in ("fwd@c4", "fwd@c3", "bwd_dkdv@c5", "bwd_dq@c5", "bwd_grads@c5"):
             r = d["kernels"][k]["roofline"]
             assert r["bound"] == "mfma" and 0 < r["frac"] < 1, k
         assert d["roofline"]["achieved"] == d["kernels"]["fwd@c4"]["roofline"]["achieved"]
