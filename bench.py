@@ -69,6 +69,9 @@ def parse_args():
                          "forward with Q rotated in registers, and dQ / dK rotated back after the backward")
     ap.add_argument("--fp8", action="store_true",
                     help="forward only, with FP8 (e4m3) Q, K, V and per-tensor scales, on the FP8 matrix cores")
+    ap.add_argument("--split-grads", action="store_true",
+                    help="backward workloads: dK/dV and dQ as two launches (the library's path for grids "
+                         "beyond two rounds of workgroup slots), each timed on its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -857,7 +860,11 @@ def main():
     dv = torch.empty(kd.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    kernels = ["fwd"] + (["bwd_preprocess", "bwd_grads"] if do_bwd else [])
+    if args.split_grads and (args.rope or not do_bwd):
+        print("--split-grads applies to backward workloads without --rope", file=sys.stderr)
+        sys.exit(2)
+    grads = ["bwd_dkdv", "bwd_dq"] if args.split_grads else ["bwd_grads"]
+    kernels = ["fwd"] + (["bwd_preprocess"] + grads if do_bwd else [])
     q_rot = k_rot = None
     if args.rope:
         # the rotated Q (kept for the backward) and K; the backward rotates dQ and dK back as
@@ -885,10 +892,16 @@ def main():
         elif do_bwd:
             gqa.gqa_attn_bwd_preprocess(o, dod, delta=delta, o_lo=o_lo, stream=stream)
             mark(2)
-            # dK, dV and dQ: one fused launch when the dK/dV grid fits in one round of
-            # workgroup slots (the default workload), else the two passes back to back
-            gqa.gqa_attn_bwd_grads(qd, kd, vd, lse, dod, delta, dq=dq, dk=dk, dv=dv, stream=stream, **kw)
-            mark(3)
+            if args.split_grads:
+                gqa.gqa_attn_bwd_dkdv(qd, kd, vd, lse, dod, delta, dk=dk, dv=dv, stream=stream, **kw)
+                mark(3)
+                gqa.gqa_attn_bwd_dq(qd, kd, vd, lse, dod, delta, dq=dq, stream=stream, **kw)
+                mark(4)
+            else:
+                # dK, dV and dQ: one fused launch when the dK/dV grid fills at most two rounds
+                # of workgroup slots, else the two passes back to back
+                gqa.gqa_attn_bwd_grads(qd, kd, vd, lse, dod, delta, dq=dq, dk=dk, dv=dv, stream=stream, **kw)
+                mark(3)
 
     warm_up(step, args.warmup, floor_s=0.0 if long_step else WARMUP_FLOOR_S)
 
@@ -917,7 +930,8 @@ def main():
     bh = w.B * w.H
     # with --rope, fwd_rope is the rotation of K plus the forward, bwd_rope delta plus dK/dV and dQ
     flop = {"fwd": 4.0 * w.D * pairs * bh, "fwd_rope": 4.0 * w.D * pairs * bh, "bwd_preprocess": 0.0,
-            "bwd_grads": 10.0 * w.D * pairs * bh, "bwd_rope": 10.0 * w.D * pairs * bh}
+            "bwd_grads": 10.0 * w.D * pairs * bh, "bwd_rope": 10.0 * w.D * pairs * bh,
+            "bwd_dkdv": 8.0 * w.D * pairs * bh, "bwd_dq": 2.0 * w.D * pairs * bh}
     elem = 2 if w.dtype in ("bf16", "f16") else 4
     hbm_bytes = {"bwd_preprocess": 3.0 * bh * w.S * w.D * elem + bh * w.S * 4}  # O, o_lo, dO in; delta out
     step_flop = flop["fwd"] + (10.0 * w.D * pairs * bh if do_bwd else 0.0)
@@ -965,7 +979,9 @@ def main():
         "config": {"workload": wl, "B": w.B, "H": w.H, "G": w.G, "S": w.S, "D": w.D, "causal": w.causal,
                    "window": w.window, "num_sinks": w.num_sinks, "visible_pairs_per_head": pairs,
                    "flop_per_step": step_flop, "parallelism": "none (1 GPU)",
-                   "rope": dict(gqa.YARN_ROPE) if args.rope else None},
+                   "rope": dict(gqa.YARN_ROPE) if args.rope else None,
+                   "grads_launches": ("two (--split-grads)" if args.split_grads else "as gqa_attn_bwd chooses")
+                   if do_bwd else None},
         "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "mfma_clock_mhz": round(clock_mhz, 1),
         "pct_of_peak_at_measured_clock": round(100 * value / (MFMA_BF16_PEAK_TFLOPS * clock_mhz / 2400.0), 2),
