@@ -421,6 +421,20 @@ def time_units(units, steps, stream):
     return per, wall_ms
 
 
+def clock_under_load(kernel, wname, probe_mhz, value, peak):
+    """The shader clock to scale the peak by: the one the counters measured during the
+    kernel's own dispatches (GRBM_GUI_ACTIVE over the dispatch time) when profiles/
+    counters.json holds them for the current sources, else the clock probe's (MFMA chains
+    right after the timed steps, not under the kernel's own power draw)."""
+    ctr = load_counters(kernel, wname)
+    if ctr and ctr.get("clock_mhz"):
+        mhz, src = ctr["clock_mhz"], f"rocprofv3 counters of {kernel}@{wname} (GRBM_GUI_ACTIVE over its dispatches)"
+    else:
+        mhz, src = probe_mhz, "gqa_clock_probe after the timed steps"
+    return {"clock_mhz_for_peak": round(mhz, 1), "clock_source": src,
+            "pct_of_peak_at_measured_clock": round(100 * value / (peak * mhz / 2400.0), 2)}
+
+
 def kernel_record(kernel, wname, ms, flop=None, nbytes=None):
     """One kernel's entry of a bench line: its event-timed milliseconds, its rate against
     its roofline (bf16 MFMA for the attention products, HBM for the delta pass), and what
@@ -539,7 +553,7 @@ def run_headline(args):
                    "also_timed": "fwd at B=1 H=128 G=16 S=16384 (causal); bwd at B=4 H=32 G=8 S=4096 (causal)"},
         "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "mfma_clock_mhz": round(clock_mhz, 1),
-        "pct_of_peak_at_measured_clock": round(100 * value / (MFMA_BF16_PEAK_TFLOPS * clock_mhz / 2400.0), 2),
+        **clock_under_load("fwd", c4.name, clock_mhz, value, MFMA_BF16_PEAK_TFLOPS),
         "mfma_busy": roofline["mfma_busy"], "hbm_gbs": roofline["hbm_gbs"],
         "kernels": kernels, "warmup_detail": notes,
         "roofline": roofline,

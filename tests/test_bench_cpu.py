@@ -152,3 +152,18 @@ def test_default_line_rejects_single_workload_flags(flag):
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), flag],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "--workload" in r.stderr
+
+
+def test_clock_under_load_prefers_the_kernels_own_counters(tmp_path, monkeypatch):
+    # the peak is scaled by the clock the counters saw during the kernel's dispatches when
+    # they match the sources, else by the probe's
+    rec = {"source_digest": bench.source_digest(), "kernels": {"fwd@c4": {"clock_mhz": 1950.0}}}
+    path = tmp_path / "counters.json"
+    path.write_text(json.dumps(rec))
+    real = bench.load_counters
+    monkeypatch.setattr(bench, "load_counters", lambda k, w, path_=str(path): real(k, w, path=path_))
+    got = bench.clock_under_load("fwd", "c4", 2100.0, 1000.0, 2516.6)
+    assert got["clock_mhz_for_peak"] == 1950.0 and "counters" in got["clock_source"]
+    assert abs(got["pct_of_peak_at_measured_clock"] - 100 * 1000.0 / (2516.6 * 1950.0 / 2400.0)) < 0.01
+    got = bench.clock_under_load("fwd", "c3", 2100.0, 1000.0, 2516.6)
+    assert got["clock_mhz_for_peak"] == 2100.0 and "probe" in got["clock_source"]

@@ -60,6 +60,7 @@ def test_bench_line(args, cpu):
             assert r["bound"] == "mfma" and 0 < r["frac"] < 1, k
         assert d["roofline"]["achieved"] == d["kernels"]["fwd@c4"]["roofline"]["achieved"]
         assert "mfma_busy" in d and "hbm_gbs" in d
+        assert d["clock_mhz_for_peak"] > 0 and d["clock_source"] and d["pct_of_peak_at_measured_clock"] > 0
         assert d["warmup_detail"]["c4"]["warmup_s"] >= 1.0
     if cpu:
         c = d["cpu_baseline"]
