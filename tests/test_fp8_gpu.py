@@ -153,3 +153,24 @@ def test_fp8_is_deterministic_and_reuses_workspace():
     o2, l2 = gqa.gqa_attn_fwd_fp8(q8, k8, v8, *sc, window=w.window, num_sinks=w.num_sinks, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_maximum_jump_inside_a_tile():
+    # The P V product takes a whole 64-key tile, so the first half's P waits in its operand
+    # while the second half is exponentiated.  Here the second half of a tile scores far above
+    # the first (2^46, then 2^92 in log2 units), which raises the running maximum between the
+    # halves: the first half's P must then enter at the old maximum, rescaled with O.
+    S = 192
+    w = Workload("fp8_jump", B=1, H=2, G=1, S=S, causal=True, seed=7300)
+    q = torch.full((1, 2, S, 64), 2.0)
+    k = torch.zeros((1, 1, S, 64))
+    k[0, 0, 32:64] = 2.0    # tile 0, second half: scores 256 against 0 before them
+    k[0, 0, 64:96] = 2.0    # tile 1, first half: at the maximum reached in tile 0
+    k[0, 0, 96:128] = 4.0   # tile 1, second half: scores 512
+    gen = torch.Generator().manual_seed(7301)
+    v = torch.randn((1, 1, S, 64), generator=gen)
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn) for x in (q, k, v))
+    sc = (1.0, 1.0, 1.0)
+    o, lse = _run(w, q8, k8, v8, sc)
+    rows = np.array([(0, h, i) for h in range(2) for i in range(S)])
+    _check_rows(w, rows, q8, k8, v8, sc, o, lse)

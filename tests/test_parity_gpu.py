@@ -354,7 +354,12 @@ def test_autograd_wrapper():
     o, lse = gqa.gqa_attention(qd, kd, vd, causal=True, sliding_window=w.window, num_sinks=w.num_sinks)
     o.backward(do.cuda())
     dQ, dK, dV = ref.backward(q, k, v, do, window=w.window, num_sinks=w.num_sinks)
-    # gradients come back in the input dtype (bf16): allow its rounding on top
-    _err("dQ", _np(qd.grad), dQ, LP_MAX + 2e-2, LP_MEAN)
-    _err("dK", _np(kd.grad), dK, LP_MAX + 2e-2, LP_MEAN)
-    _err("dV", _np(vd.grad), dV, LP_MAX + 2e-2, LP_MEAN)
+    # autograd hands the gradients back in the inputs' dtype (bf16): the library's fp32
+    # gradients meet the stated bar, and rounding to bf16 adds at most half a bf16 ulp,
+    # 2^-8 |x|, element by element on top of it
+    for name, got, want in (("dQ", qd.grad, dQ), ("dK", kd.grad, dK), ("dV", vd.grad, dV)):
+        g, x = _np(got), np.asarray(want, dtype=np.float64)
+        excess = np.abs(g - x) - 2.0 ** -8 * np.abs(x)  # error beyond the rounding to bf16
+        print(f"  {name}: max error beyond bf16 rounding {excess.max():.3e}", flush=True)
+        assert excess.max() <= LP_MAX, f"{name}: {excess.max():.3e} beyond the bar plus bf16 rounding"
+        _err(name, g, x, np.inf, LP_MEAN)

@@ -9,7 +9,9 @@
 // decomposition, tile ranges, masks and the lazy online softmax are those of the bf16
 // forward (gqa_fwd.hip), with one change: P must stay below e4m3's 448, so a half goes
 // through the exact maximum path when a lane's partial row sum exceeds 256 (not 2^16);
-// after that path every P is at most 2^8.
+// after that path every P is at most 2^8.  And the P V product takes the whole tile, so
+// when the second half raises the maximum, the first half's P (still waiting in the
+// operand, at the old maximum) is added to O before the rescale (see decide).
 //
 // Operand order.  A 32x32x64 operand gives each lane 32 bytes of one row (lane % 32) for
 // one k-group (lane / 32); the instruction pairs element i of group g of both operands,
@@ -110,7 +112,12 @@ struct Fp8Wave {
     }
   }
 
-  __device__ __forceinline__ void decide(const f32x16 (&s)[2]) {
+  // H = 1: the first half's P already sits in bytes 0..15 of the P operands at the old
+  // maximum, waiting for the tile's P V; when the maximum is raised, that half is added to
+  // O first (a P V with the second half's bytes zero) so that the rescale covers it, and
+  // its bytes are cleared, so the tile's P V adds the second half alone.
+  template <int H>
+  __device__ __forceinline__ void decide(const f32x16 (&s)[2], i32x8 (&pf)[2], const i32x8 (&va)[2]) {
     float mx[2];
     bool need = false;
 #pragma unroll
@@ -132,6 +139,20 @@ struct Fp8Wave {
         mrow[cb] = mnew;
         nmuse[cb] = mnew == -INFINITY ? 0.f : -mnew;
         lrow[cb] *= alpha[cb];
+      }
+      if constexpr (H == 1) {
+        i32x8 p0[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          p0[cb] = pf[cb];
+#pragma unroll
+          for (int w = 4; w < 8; ++w) p0[cb][w] = 0;
+        }
+        accumulate(va, p0);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pf[cb][w] = 0;
       }
       apply_rescale();
     }
@@ -157,13 +178,13 @@ struct Fp8Wave {
   }
 
   template <int H>
-  __device__ __forceinline__ void softmax_half(const f32x16 (&s)[2], i32x8 (&pf)[2]) {
+  __device__ __forceinline__ void softmax_half(const f32x16 (&s)[2], i32x8 (&pf)[2], const i32x8 (&va)[2]) {
     float ls[2];
     probs<H>(s, pf, ls);
     const bool need = !(ls[0] <= kSumGuard8) | !(ls[1] <= kSumGuard8) | ((mrow[0] == -INFINITY) & (q0 + l32 < m.S)) |
                       ((mrow[1] == -INFINITY) & (q0 + 32 + l32 < m.S));
     if (__builtin_expect(wave_any(need), 0)) {
-      decide(s);
+      decide<H>(s, pf, va);
       probs<H>(s, pf, ls);
     }
     lrow[0] += ls[0];
@@ -296,11 +317,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
     const i32x8 va[2] = {W.operand(vn, 0), W.operand(vn, 1)};
     ka = W.operand(kn1, 0);
     if (__builtin_expect(!W.half_full(k0), 0)) W.mask(sc, k0);
-    W.softmax_half<0>(sc, pf);
+    W.softmax_half<0>(sc, pf, va);
     W.scores(ka, sc);                       // S(n + 1, 0)
     ka = W.operand(kn1, 1);
     if (__builtin_expect(!W.half_full(k0 + 32), 0)) W.mask(sn, k0 + 32);
-    W.softmax_half<1>(sn, pf);
+    W.softmax_half<1>(sn, pf, va);
     W.accumulate(va, pf);
     lds_barrier8<0>();
   };
