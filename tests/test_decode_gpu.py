@@ -76,3 +76,25 @@ def test_decode_is_deterministic_and_reuses_workspace():
     o2, l2 = gqa.gqa_attn_decode(q, k, v, window=w.window, num_sinks=w.num_sinks, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("sq", [1, 16])
+def test_decode_maximum_jumps_inside_tiles(sq):
+    # cache keys whose scores jump by 2^46, then 2^92 (log2 units) between the halves of a
+    # 64-key tile: every partial's running maximum is raised in the middle of a tile
+    B, H, G, Skv = 1, 8, 1, 320
+    q = torch.full((B, H, sq, 64), 2.0)
+    k = torch.zeros((B, G, Skv, 64))
+    k[:, :, 32:64] = 2.0
+    k[:, :, 64:96] = 2.0
+    k[:, :, 96:128] = 4.0
+    v = torch.randn((B, G, Skv, 64), generator=torch.Generator().manual_seed(7320))
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    o, lse = gqa.gqa_attn_decode(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    O, L = ref.decode(q, k, v)
+    eo = np.abs(o.float().cpu().numpy().astype(np.float64) - O)
+    el = np.abs(lse.cpu().numpy().astype(np.float64) - L)
+    print(f"  O: max {eo.max():.3e} mean {eo.mean():.3e}; lse: max {el.max():.3e}", flush=True)
+    assert np.isfinite(eo).all() and np.isfinite(el).all()
+    assert eo.max() <= O_MAX and eo.mean() <= O_MEAN and el.max() <= LSE_MAX

@@ -363,3 +363,33 @@ def test_autograd_wrapper():
         print(f"  {name}: max error beyond bf16 rounding {excess.max():.3e}", flush=True)
         assert excess.max() <= LP_MAX, f"{name}: {excess.max():.3e} beyond the bar plus bf16 rounding"
         _err(name, g, x, np.inf, LP_MEAN)
+
+
+def _jump_inputs(B, H, G, S, dtype=torch.bfloat16, seed=7311):
+    """q = 2 everywhere; K zero except key blocks whose scores jump by 2^46 and then 2^92
+    (log2 units at scale 1/8) in the middle of 64-key tiles; V random.  Exact in bf16."""
+    q = torch.full((B, H, S, 64), 2.0)
+    k = torch.zeros((B, G, S, 64))
+    k[:, :, 32:64] = 2.0
+    k[:, :, 64:96] = 2.0
+    k[:, :, 96:128] = 4.0
+    v = torch.randn((B, G, S, 64), generator=torch.Generator().manual_seed(seed))
+    return tuple(x.to(dtype) for x in (q, k, v))
+
+
+def test_maximum_jumps_inside_tiles():
+    # the lazy running maximum meets scores that jump far above it between the 32-key halves
+    # of a tile and between tiles; each unit that raises it must rescale what came before
+    w = Workload("jump", B=1, H=2, G=1, S=192, direction="fwd+bwd", seed=7310)
+    q, k, v = _jump_inputs(w.B, w.H, w.G, w.S)
+    (qd, kd, vd), o, lse = run_fwd(w, q, k, v)
+    O, L = ref.forward(q, k, v, scale=w.scale, causal=True)
+    _err("O", _np(o), O, LP_MAX, LP_MEAN)
+    _err("lse", _np(lse), L, LSE_MAX)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(7312)).to(torch.bfloat16)
+    dq, dk, dv = gqa.gqa_attn_bwd(qd, kd, vd, o, lse, do.cuda(), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    dQ, dK, dV = ref.backward(q, k, v, do, scale=w.scale, causal=True)
+    _err("dQ", _np(dq), dQ, LP_MAX, LP_MEAN)
+    _err("dK", _np(dk), dK, LP_MAX, LP_MEAN)
+    _err("dV", _np(dv), dV, LP_MAX, LP_MEAN)
