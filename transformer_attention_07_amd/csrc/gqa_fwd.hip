@@ -12,19 +12,20 @@
 // Per wave, S^T = K Q^T runs on v_mfma_f32_32x32x16 with the wave's Q tile held in
 // registers as the B operand, so each accumulator lane holds one query column: row
 // statistics are in-lane plus one exchange between the two 32-lane halves.  The loop is a
-// software pipeline over 32-key halves: while the VALU exponentiates one half, the matrix
-// cores compute the scores of the next, then the half's probabilities feed
-// O^T += V^T P^T.  Operands are read from LDS one step ahead of their MFMAs.  V^T
-// operands come from the row-major V tile through ds_read_b64_tr_b16 transposed reads, and
-// P^T straight from the S^T accumulator registers (see gqa_device.h).
+// software pipeline over units of one 32-key half and one 32-row column block: while the
+// VALU exponentiates one unit, the matrix cores compute the previous unit's
+// O^T += V^T P^T and the next unit's scores, so the compiler can interleave the two inside
+// the wave.  Operands are read from LDS a unit or two ahead of their MFMAs.  V^T operands
+// come from the row-major V tile through ds_read_b64_tr_b16 transposed reads, and P^T
+// straight from the S^T accumulator registers (see gqa_device.h).
 //
 // Online softmax in fp32: exp2 with scale*log2(e) folded into one FMA and row sums of the
 // unrounded P in fp32 (so lse keeps fp32 accuracy).  The running maximum only keeps exp2
-// in range, so a half is exponentiated against it without computing the half's own
+// in range, so a unit is exponentiated against it without computing the unit's own
 // maximum; a lane's partial row sum above 2^16 (or a row with no maximum yet) sends the
-// half through the exact path: take its maximum, raise the running maximum when it grew by
+// unit through the exact path: take its maximum, raise the running maximum when it grew by
 // more than 2^8, rescale O and the sums, exponentiate again.  P thus stays below 2^16,
-// which the rounded operands and fp32 sums carry at full relative precision.  Halves that
+// which the rounded operands and fp32 sums carry at full relative precision.  Units that
 // are not fully visible are masked with one compare per element against per-lane bounds.
 //
 // The online softmax with running max and sum and the fused score/softmax/PV loop follow
@@ -39,9 +40,9 @@ namespace gqa {
 namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
-// A half's exponentials are taken against the running maximum without looking at the
-// half's own maximum; if a lane's partial row sum exceeds this (some P > 2^16 / 16, or an
-// overflow), the half is redone after a proper maximum decision.
+// A unit's exponentials are taken against the running maximum without looking at the
+// unit's own maximum; if a lane's partial row sum exceeds this (some P > 2^16 / 16, or an
+// overflow), the unit is redone after a proper maximum decision.
 constexpr float kSumGuard = 65536.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
