@@ -21,6 +21,7 @@ CASES = [
     ([], True),                       # the default line, with the CPU baseline
     (["--workload", "step"], False),
     (["--workload", "c5"], False),
+    (["--workload", "c5", "--split-grads"], False),
     (["--workload", "c3"], False),
     (["--workload", "decode16"], False),
     (["--workload", "rope_k"], False),
@@ -62,6 +63,9 @@ def test_bench_line(args, cpu):
         assert "mfma_busy" in d and "hbm_gbs" in d
         assert d["clock_mhz_for_peak"] > 0 and d["clock_source"] and d["pct_of_peak_at_measured_clock"] > 0
         assert d["warmup_detail"]["c4"]["warmup_s"] >= 1.0
+    if "--split-grads" in args:
+        assert d["kernels"]["bwd_dkdv"]["ms"] > 0 and d["kernels"]["bwd_dq"]["ms"] > 0
+        assert "bwd_grads" not in d["kernels"] and "two" in d["config"]["grads_launches"]
     if cpu:
         c = d["cpu_baseline"]
         assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
