@@ -44,6 +44,12 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 // unit's own maximum; if a lane's partial row sum exceeds this (some P > 2^16 / 16, or an
 // overflow), the unit is redone after a proper maximum decision.
 constexpr float kSumGuard = 65536.0f;
+// The running maximum of a row that has seen no visible key yet: a finite value below every
+// score (log2 units) the kernel meets, so that its first visible key gives exp2 of about
+// 10^38 = inf, which the row-sum guard sends through the exact path; masked keys (-inf)
+// still give 0.  (Scores below -10^38 in log2 units, i.e. past fp32's range at the default
+// scale, would need the old explicit test.)
+constexpr float kNoMax = -1.0e38f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Per-wave state and the pieces of one key tile.  The loop works in units of one 32-key
@@ -56,9 +62,9 @@ struct FwdWave {
   float c2;
   u32x4 qf[2][4];   // Q tile as B operands [column block][contraction step]
   f32x16 o[2][2];   // O^T accumulators [d block][column block]
-  float mrow[2];    // running maximum (log2 units) per column block
+  float mrow[2];    // running maximum (log2 units) per column block; kNoMax before any key
   float lrow[2];    // running sum (this lane's half of the keys)
-  float nmuse[2];   // -mrow, or 0 while the row has seen no visible key (mrow = -inf)
+  float nmuse[2];   // -mrow
   int lim_hi;       // a key half [k, k + 31] is fully visible to all 64 rows iff
   int win_lo;       //   k + 31 <= lim_hi && (k >= win_lo || k + 31 < m.sinks)
   int koff[4];      // lane's byte offset of the K operand, contraction step ks (block 0)
@@ -153,10 +159,10 @@ struct FwdWave {
     auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     const float mx = vmax(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1])) * c2;
     if (__builtin_expect(wave_any(mx > mrow[CB] + kRescaleThreshold), 0)) {
-      const float mnew = vmax(mrow[CB], mx);
-      const float alpha = mnew != -INFINITY ? exp2_fast(mrow[CB] - mnew) : 1.0f;
+      const float mnew = vmax(mrow[CB], mx);  // finite: mrow starts at kNoMax
+      const float alpha = exp2_fast(mrow[CB] - mnew);
       mrow[CB] = mnew;
-      nmuse[CB] = mnew == -INFINITY ? 0.f : -mnew;
+      nmuse[CB] = -mnew;
       lrow[CB] *= alpha;
       // keep this block a real branch: O *= 1 is an identity, and hoisting the multiplies
       // out of the (rare) branch would put them on every step
@@ -186,17 +192,15 @@ struct FwdWave {
 
   // Softmax of one (masked) unit against the running maximum.  The maximum only serves to
   // keep exp2 in range, so it is left alone unless a lane's partial row sum shows an
-  // exponent above log2(kSumGuard / 16) or the row has no maximum yet (no visible key so
-  // far); then the unit's maximum is taken (decide, which raises it and rescales O and the
-  // row sums) and the unit is exponentiated again.  P therefore stays below 2^16: the
-  // rounded operands and fp32 sums keep their relative precision at any magnitude.  (Rows
-  // past the end of the sequence may never see a key; they do not hold the slow path.)
+  // exponent above log2(kSumGuard / 16) (which includes a row's first visible key, against
+  // kNoMax); then the unit's maximum is taken (decide, which raises it and rescales O and
+  // the row sums) and the unit is exponentiated again.  P therefore stays below 2^16: the
+  // rounded operands and fp32 sums keep their relative precision at any magnitude.
   template <int CB>
   __device__ __forceinline__ void softmax(const f32x16& s, u32x4 (&pf)[2]) {
     float ls;
     probs<CB>(s, pf, ls);
-    // bitwise combination: one ballot, no per-lane branches
-    const bool need = !(ls <= kSumGuard) | ((mrow[CB] == -INFINITY) & (q0 + CB * 32 + l32 < m.S));
+    const bool need = !(ls <= kSumGuard);
     if (__builtin_expect(wave_any(need), 0)) {
       decide<CB>(s);
       probs<CB>(s, pf, ls);
@@ -332,9 +336,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) W.o[db][cb] = f32x16{};
-  W.mrow[0] = W.mrow[1] = -INFINITY;
+  W.mrow[0] = W.mrow[1] = kNoMax;
   W.lrow[0] = W.lrow[1] = 0.f;
-  W.nmuse[0] = W.nmuse[1] = 0.f;
+  W.nmuse[0] = W.nmuse[1] = -kNoMax;
   W.lim_hi = __builtin_amdgcn_readfirstlane(W.m.causal ? imin(W.q0, S - 1) : S - 1);
   W.win_lo = __builtin_amdgcn_readfirstlane(W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30));
 
