@@ -489,10 +489,12 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
 }
 
 // One wave per output row (b, h, t): lane = d.  O = sum_p w_p O_p / sum_p w_p l_p with
-// w_p = 2^(m_p - max_p m_p); lse = (max_p m_p + log2 sum_p w_p l_p) ln 2.  Lane j holds
-// the maximum and sum of partial c + j of a chunk of 64 partials; the weights reach every
-// lane through readlane, and each step issues the loads of 16 partials' O before their
-// multiply-adds, so the loads are in flight together.
+// w_p = 2^(m_p - max_p m_p); lse = (max_p m_p + log2 sum_p w_p l_p) ln 2.  The partials
+// go in groups of kMergeGroup: lane j loads the maximum and sum of partial c + j while
+// every lane loads its element of all the group's O rows, all in one round trip (the
+// work is a few KB per row, so latency, not bandwidth, sets its time); the weights reach
+// every lane through readlane.  Between groups the running maximum, sum and O are
+// rescaled as in the online softmax.
 template <int DT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -507,35 +509,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int n_part = p.n_part;
   const float* ml = p.part_ml + (size_t)set * n_part * 2 * kDecodeRows + rr;
   const float* po = p.part_o + ((size_t)set * n_part * kDecodeRows + rr) * kHeadDim + lane;
-  auto part_m = [&](int i) __attribute__((always_inline)) {
-    return i < n_part ? ml[(size_t)i * 2 * kDecodeRows] : -INFINITY;
-  };
-  float mstar = -INFINITY;
-  for (int c = 0; c < n_part; c += 64) mstar = vmax(mstar, part_m(c + lane));
+  constexpr int kMergeGroup = 32;
+  float mrun = -INFINITY, L = 0.f, acc = 0.f;
+  for (int c = 0; c < n_part; c += kMergeGroup) {
+    const int cnt = imin(kMergeGroup, n_part - c);
+    const bool mine = lane < cnt;
+    const float mi = mine ? ml[(size_t)(c + lane) * 2 * kDecodeRows] : -INFINITY;
+    const float li = mine ? ml[(size_t)(c + lane) * 2 * kDecodeRows + kDecodeRows] : 0.f;
+    float ov[kMergeGroup];
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) mstar = vmax(mstar, __shfl_xor(mstar, s, 64));
-  float L = 0.f, acc = 0.f;
-  for (int c = 0; c < n_part; c += 64) {
-    const int i = c + lane;
-    const float mi = part_m(i);
-    const float w = mi == -INFINITY ? 0.f : exp2_fast(mi - mstar);
-    L += i < n_part ? w * ml[(size_t)i * 2 * kDecodeRows + kDecodeRows] : 0.f;
-    const int cnt = imin(64, n_part - c);
+    for (int u = 0; u < kMergeGroup; ++u) ov[u] = u < cnt ? po[(size_t)(c + u) * kDecodeRows * kHeadDim] : 0.f;
+    float mg = mi;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) mg = vmax(mg, __shfl_xor(mg, s, 64));
+    const float mnew = vmax(mrun, mg);
+    // a partial (or the groups so far) with no visible key has maximum -inf and weight 0
+    const float keep = mrun == -INFINITY ? 0.f : exp2_fast(mrun - mnew);
+    const float w = mi == -INFINITY ? 0.f : exp2_fast(mi - mnew);
+    float wl = w * li;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) wl += __shfl_xor(wl, s, 64);
+    L = L * keep + wl;
+    acc *= keep;
     const int wbits = __builtin_bit_cast(int, w);
-    for (int j0 = 0; j0 < cnt; j0 += 16) {
-      float ov[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) ov[u] = j0 + u < cnt ? po[(size_t)(c + j0 + u) * kDecodeRows * kHeadDim] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, j0 + u)) * ov[u];
-    }
+    for (int u = 0; u < kMergeGroup; ++u)
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, u)) * ov[u];
+    mrun = mnew;
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) L += __shfl_xor(L, s, 64);
   const float out = acc / L;
   ((uint16_t*)p.o)[row * kHeadDim + lane] = (uint16_t)(pack2<DT>(out, 0.f) & 0xFFFFu);
-  if (lane == 0) p.lse[row] = (mstar + log2f(L)) * kLn2;
+  if (lane == 0) p.lse[row] = (mrun + log2f(L)) * kLn2;
 }
 
 template <int DT>
