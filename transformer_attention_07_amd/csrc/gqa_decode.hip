@@ -62,6 +62,13 @@ __device__ __forceinline__ void wait_counts() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LG << 8) | (((VM >> 4) & 3) << 14));
 }
 
+// One direct load of 16 bytes per lane into LDS at dst + 16 lane.  (A plain function: the
+// builtin called straight from a generic lambda makes the host pass drop the kernel's
+// launch stub without a diagnostic.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, lds_char* dst, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
 // One 64-key tile (K and V row-major in LDS, rows k0 ..) against NB 32-row blocks of query
 // rows held as B operands: S^T = K Q^T, the online-softmax update (exact maximum, rescale of
 // O and of the row sum), O^T += V^T P^T.  `full`: every pair of the tile is visible, no mask.
@@ -317,19 +324,18 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
 // each tile.  The workgroup is one partial (split) over every nsplit-th tile of the list;
 // the tiles pass through a ring of kSharedStages LDS buffers filled by all waves together
 // (each issues the direct loads j with j % NRB == wave), one barrier per tile.
-constexpr int kSharedStages = 4;
+constexpr int kSharedStages = 5;
 
 // The ring's buffers, each a distinct LDS object selected at compile time, so that every
 // LDS address is a known constant (typed LDS pointers from here on: no generic pointer is
-// ever cast back to LDS).
-__shared__ __attribute__((aligned(1024))) char g_dec_k0[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_k1[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_k2[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_k3[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_v0[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_v1[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_v2[8192];
-__shared__ __attribute__((aligned(1024))) char g_dec_v3[8192];
+// ever cast back to LDS).  A stage holds a tile's K (bytes 0..8191) and V (8192..16383):
+// one object per stage keeps the direct loads in flight within the compiler's count of
+// LDS objects it tells apart (more objects and it waits for every load before some reads).
+__shared__ __attribute__((aligned(1024))) char g_dec_t0[16384];
+__shared__ __attribute__((aligned(1024))) char g_dec_t1[16384];
+__shared__ __attribute__((aligned(1024))) char g_dec_t2[16384];
+__shared__ __attribute__((aligned(1024))) char g_dec_t3[16384];
+__shared__ __attribute__((aligned(1024))) char g_dec_t4[16384];
 // f(integral_constant<int, U>) for U = B .. E - 1, in order
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -342,22 +348,125 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int U>
 __device__ __forceinline__ lds_char* ring_k() {
   static_assert(U >= 0 && U < kSharedStages, "ring slot");
-  if constexpr (U == 0) return (lds_char*)g_dec_k0;
-  else if constexpr (U == 1) return (lds_char*)g_dec_k1;
-  else if constexpr (U == 2) return (lds_char*)g_dec_k2;
-  else return (lds_char*)g_dec_k3;
+  if constexpr (U == 0) return (lds_char*)g_dec_t0;
+  else if constexpr (U == 1) return (lds_char*)g_dec_t1;
+  else if constexpr (U == 2) return (lds_char*)g_dec_t2;
+  else if constexpr (U == 3) return (lds_char*)g_dec_t3;
+  else return (lds_char*)g_dec_t4;
 }
 template <int U>
 __device__ __forceinline__ lds_char* ring_v() {
-  static_assert(U >= 0 && U < kSharedStages, "ring slot");
-  if constexpr (U == 0) return (lds_char*)g_dec_v0;
-  else if constexpr (U == 1) return (lds_char*)g_dec_v1;
-  else if constexpr (U == 2) return (lds_char*)g_dec_v2;
-  else return (lds_char*)g_dec_v3;
+  return ring_k<U>() + 8192;
 }
 
+// The running maximum of a row before its first visible key: a finite value below every
+// score (log2 units), so that the first visible key exponentiates to +inf and the row-sum
+// guard takes the exact path; masked keys (-inf) still give 0.  A partial that never sees
+// a key keeps it, and its merge weight 2^(-1e38 - m) is 0.
+constexpr float kDecodeNoMax = -1.0e38f;
+
+// One wave's 32 query rows (lane column l32 = row) in the shared-tile kernel, worked in
+// units of one 32-key half of a tile: S^T = K Q^T on MFMA, the online softmax with the lazy
+// maximum, O^T += V^T P^T.  Row r of the wave sits at position pos (-1: no row).
+template <int DT>
+struct DecWave {
+  int hl;
+  int pos;
+  float c2;
+  u32x4 qf[4];     // the rows as B operands [contraction step]
+  f32x16 o[2];     // O^T accumulators [d block]
+  float mrow;      // running maximum (log2 units), kDecodeNoMax before any key
+  float lrow;      // running sum (this lane's half of the keys)
+  float nmuse;     // -mrow
+  int koff[4];     // lane's byte offset of the K operand, step ks (half 0)
+  int voff[2][2];  // lane's byte offset of the transposed V read [d block][second row group]
+
+  __device__ __forceinline__ void load_k(const lds_char* kt, int kb, u32x4 (&a)[4]) const {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = *(const lds_u32x4*)(kt + kb * 4096 + koff[ks]);
+  }
+  __device__ __forceinline__ void scores(const u32x4 (&a)[4], f32x16& s) const {
+    s = mfma32<DT>(a[0], qf[0], f32x16{});
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) s = mfma32<DT>(a[ks], qf[ks], s);
+  }
+  __device__ __forceinline__ void load_v(const lds_char* vt, int kb, u32x4 (&a)[2][2]) const {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const lds_char* base = vt + (kb * 32 + 16 * t) * 128;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[db][0]));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[db][1]));
+        const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+        a[db][t] = u32x4{ux[0], ux[1], uy[0], uy[1]};
+      }
+  }
+  __device__ __forceinline__ void accumulate(const u32x4 (&a)[2][2], const u32x4 (&pf)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] = mfma32<DT>(a[db][t], pf[t], o[db]);
+  }
+  // hide the keys of half [k, k + 31] this lane's row does not see: register r holds key
+  // k + 4 hl + 8 (r / 4) + r % 4
+  __device__ __forceinline__ void mask(f32x16& s, int k, int Skv, int W, int NS) const {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = k + 8 * (r >> 2) + 4 * hl + (r & 3);
+      const bool vis = (j <= pos) & (j < Skv) & ((W == 0) | (j > pos - W) | (j < NS));
+      s[r] = vis ? s[r] : -INFINITY;
+    }
+  }
+  // raise the running maximum when the unit's exceeds it by more than kDecodeRescale (rare)
+  __device__ __forceinline__ void decide(const f32x16& s) {
+    float a = vmax(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) a = vmax(vmax(a, s[r]), s[r + 1]);
+    const float mx = max_across_halves(a) * c2;
+    if (__builtin_expect(wave_any(mx > mrow + kDecodeRescale), 0)) {
+      const float mnew = vmax(mrow, mx);  // finite: mrow starts at kDecodeNoMax
+      const float alpha = exp2_fast(mrow - mnew);
+      mrow = mnew;
+      nmuse = -mnew;
+      lrow *= alpha;
+      asm volatile("" ::: "memory");  // keep the rescale inside this rare branch
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] *= alpha;
+    }
+  }
+  __device__ __forceinline__ void probs(const f32x16& s, u32x4 (&pf)[2], float& ls) const {
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[8 * t + e], c2, nmuse));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pf[t][w] = pack2<DT>(pv[2 * w], pv[2 * w + 1]);
+        lsum += pv[2 * w] + pv[2 * w + 1];
+      }
+    }
+    ls = lsum;
+  }
+  // Lazy maximum, as in the prefill forward: the unit is exponentiated against the running
+  // maximum, which only keeps exp2 in range; a lane's partial row sum above the guard (an
+  // exponent above log2(guard / 16), the row's first visible key included) sends it
+  // through the exact path.
+  __device__ __forceinline__ void softmax(const f32x16& s, u32x4 (&pf)[2]) {
+    float ls;
+    probs(s, pf, ls);
+    if (__builtin_expect(wave_any(!(ls <= kDecodeSumGuard)), 0)) {
+      decide(s);
+      probs(s, pf, ls);
+    }
+    lrow += ls;
+  }
+};
+
 template <int DT, int NRB>
-__global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * NRB, NRB > 2 ? 2 : 1) void decode_shared_kernel(DecodeParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = row block
@@ -372,105 +481,155 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
   const int part = split;
   const int Skv = p.Skv, Sq = p.Sq;
   const int W = p.mask.window, NS = p.mask.sinks;
-  const float c2 = p.scale_log2;
   const int nt = p.tiles.count();
   const int my_nt = nt > part ? (nt - 1 - part) / n_part + 1 : 0;
 
-  // this wave's rows: r = rc * 128 + 32 wave + l32
-  u32x4 qf[1][4];
-  int pos[1];
+  DecWave<DT> D;
+  D.hl = hl;
+  D.c2 = p.scale_log2;
   {
+    // this wave's rows: r = rc * 128 + 32 wave + l32
     const int r = rc * kDecodeRows + wave * 32 + l32;
     const bool ok = r < p.rows;
     const int hh = ok ? r / Sq : 0, t = ok ? r % Sq : 0;
-    pos[0] = ok ? Skv - Sq + t : -1;
+    D.pos = ok ? Skv - Sq + t : -1;
     const uint16_t* qrow = (const uint16_t*)p.q + ((size_t)(b * p.H + g * p.hpg + hh) * Sq + t) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qf[0][ks] = ok ? *(const u32x4*)(qrow + ks * 16 + hl * 8) : u32x4{0u, 0u, 0u, 0u};
+      D.qf[ks] = ok ? *(const u32x4*)(qrow + ks * 16 + hl * 8) : u32x4{0u, 0u, 0u, 0u};
   }
   const bool rows_full = rc * kDecodeRows + NRB * 32 <= p.rows;
-
-  int koff[4], voff[2][2], soff[8];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) koff[ks] = rm_off(l32, ks * 2 + hl);
+  for (int ks = 0; ks < 4; ++ks) D.koff[ks] = rm_off(l32, ks * 2 + hl);
   {
     const int r0 = 4 * hl + ((lane & 15) >> 2);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int c0 = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff[db][0] = rm_off(r0, c0 >> 3) + (c0 & 7) * 2;
-      voff[db][1] = rm_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
+      D.voff[db][0] = rm_off(r0, c0 >> 3) + (c0 & 7) * 2;
+      D.voff[db][1] = rm_off(r0 + 8, c0 >> 3) + (c0 & 7) * 2;
     }
   }
+  // global offsets of this wave's direct loads inside a tile's rows: load wave + NRB u of
+  // the K rows and the same of the V rows (NRB dividing 16), else all eight
+  constexpr int kOwn = 16 % NRB == 0 ? 8 / NRB : 8;
+  int soff[kOwn];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) soff[j] = stage_voff(j, lane);
+  for (int u = 0; u < kOwn; ++u) soff[u] = stage_voff(16 % NRB == 0 ? wave + NRB * u : u, lane);
+  D.o[0] = D.o[1] = f32x16{};
+  D.mrow = kDecodeNoMax;
+  D.nmuse = -kDecodeNoMax;
+  D.lrow = 0.f;
 
   const size_t slab = (size_t)bg * Skv * kHeadDim;
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const uint16_t*)p.k + slab, Skv);
   const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const uint16_t*)p.v + slab, Skv);
+  // rows of this workgroup's tile i; past its last tile, row Skv: loads read zeros
   auto tile_row = [&](int i) __attribute__((always_inline)) {
     return i < my_nt ? p.tiles.tile(part + i * n_part) * kTile : Skv;
   };
-  // this wave's share of the tile's 16 direct loads (8 K, 8 V)
-  auto stage = [&](lds_char* kt, lds_char* vt, int row0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j % NRB == wave) {
-        if (j < 8)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + 1024 * j), 16, row0 * 128 + soff[j], 0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vt + 1024 * (j - 8)), 16,
-                                                   row0 * 128 + soff[j - 8], 0, 0, 0);
-      }
+  // every row of the chunk sees every key of half [k, k + 31]
+  auto half_full = [&](int k) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane((int)rows_full & (int)(k + 31 <= Skv - Sq) &
+                                          ((int)(W == 0) | (int)(k > Skv - 1 - W) | (int)(k + 31 < NS))) != 0;
   };
-  // loads per tile of the wave with the fewest: with kSharedStages - 1 tiles in flight,
-  // waiting until at most kSharedStages - 2 tiles' worth are outstanding guarantees that
-  // this wave's loads of the oldest staged tile have landed
+  // this wave's share of the tile's 16 direct loads (8 K, 8 V): loads wave + NRB u.  Each
+  // load sits at a compile-time LDS offset (one branch per wave index), so the compiler
+  // knows which buffer every load in flight writes.
+  auto stage = [&](lds_char* kt, lds_char* vt, int row0) __attribute__((always_inline)) {
+    if constexpr (16 % NRB == 0) {
+      static_for<0, NRB>([&](auto wv) __attribute__((always_inline)) {
+        constexpr int WV = decltype(wv)::value;
+        if (wave == WV) {
+#pragma unroll
+          for (int u = 0; u < kOwn; ++u) lds_load16(krs, kt + 1024 * (WV + NRB * u), row0 * 128 + soff[u]);
+#pragma unroll
+          for (int u = 0; u < kOwn; ++u) lds_load16(vrs, vt + 1024 * (WV + NRB * u), row0 * 128 + soff[u]);
+        }
+      });
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j % NRB == wave) {
+          if (j < 8)
+            lds_load16(krs, kt + 1024 * j, row0 * 128 + soff[j]);
+          else
+            lds_load16(vrs, vt + 1024 * (j - 8), row0 * 128 + soff[j - 8]);
+        }
+    }
+  };
+  // loads per tile of the wave with the fewest: waiting until at most two tiles' worth are
+  // outstanding guarantees that this wave's loads of the oldest of three have landed
   constexpr int kMinPerTile = 16 / NRB;
 
-  f32x16 o[1][2];
-  float m[1], l[1];
-  o[0][0] = o[0][1] = f32x16{};
-  m[0] = -INFINITY;
-  l[0] = 0.f;
-
+  // Software pipeline over units (one 32-key half): a unit's softmax runs while the
+  // matrix cores compute the previous unit's P V and the next unit's scores, three
+  // independent pieces the compiler interleaves inside the wave.  Tile i's two units
+  // read the scores of (i, 1) and (i + 1, 0), so tile i + 1 must have landed when tile
+  // i starts: iteration i waits for this wave's loads of tile i + 1, then a barrier (every
+  // wave's loads of tile i + 1 have landed; every wave is done with tile i - 1, whose
+  // second V half the previous unit read), then loads tile i + 4 into tile i - 1's
+  // buffer.  Three tiles are in flight during the wait.
   static_for<0, kSharedStages - 1>([&](auto u) __attribute__((always_inline)) {
     constexpr int U = decltype(u)::value;
     stage(ring_k<U>(), ring_v<U>(), tile_row(U));
   });
-  // Tile i: wait for this wave's loads of tile i, barrier (every wave's loads of tile i have
-  // landed and every wave is done with tile i - 1), load tile i + kSharedStages - 1 into
-  // tile i - 1's buffer, compute tile i.
+  f32x16 sx, sy;               // S^T of the units at half 0 / half 1
+  u32x4 ka0[4], ka1[4];        // K operands of half 0 / half 1
+  u32x4 va0[2][2], va1[2][2];  // V^T operands of half 0 / half 1
+  u32x4 px[2], py[2];          // P^T of the units from sx / sy
+  wait_counts<(kSharedStages - 2) * kMinPerTile, 0>();  // tile 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  D.load_k(ring_k<0>(), 0, ka0);
+  D.scores(ka0, sx);
+  D.load_k(ring_k<0>(), 1, ka1);
+  // the first unit's P V (of no earlier unit) adds zero
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    py[t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < 2; ++db) va1[db][t] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Step i: the wait, barrier and loads run on every step of the last round too (past the
+  // end they load zeros, with no memory traffic), so that every path through the loop has
+  // the same loads in flight; only the units are skipped past the last tile.
   auto body = [&](auto par, int i) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    constexpr int F = (P + kSharedStages - 1) % kSharedStages;
+    constexpr int P1 = (P + 1) % kSharedStages;                  // tile i + 1
+    constexpr int F = (P + kSharedStages - 1) % kSharedStages;   // tile i - 1, receives i + 4
     asm volatile("" ::: "memory");
-    wait_counts<(kSharedStages - 2) * kMinPerTile, 0>();
+    wait_counts<(kSharedStages - 3) * kMinPerTile, 0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     stage(ring_k<F>(), ring_v<F>(), tile_row(i + kSharedStages - 1));
+    if (i >= my_nt) return;
     const int k0 = tile_row(i);
-    const bool full = __builtin_amdgcn_readfirstlane(
-                          (int)rows_full & (int)(k0 + 63 <= Skv - Sq) &
-                          ((int)(W == 0) | (int)(k0 > Skv - 1 - W) | (int)(k0 + 63 < NS))) != 0;
-    decode_tile<DT, 1>(ring_k<P>(), ring_v<P>(), k0, full, qf, pos, o, m, l, koff, voff, hl, c2, Skv, W, NS);
+    // (i, 0) from sx; P V of (i - 1, 1); scores of (i, 1)
+    if (__builtin_expect(!half_full(k0), 0)) D.mask(sx, k0, Skv, W, NS);
+    D.accumulate(va1, py);
+    D.scores(ka1, sy);
+    D.load_k(ring_k<P1>(), 0, ka0);
+    D.load_v(ring_v<P>(), 0, va0);
+    D.softmax(sx, px);
+    // (i, 1) from sy; P V of (i, 0); scores of (i + 1, 0)
+    if (__builtin_expect(!half_full(k0 + 32), 0)) D.mask(sy, k0 + 32, Skv, W, NS);
+    D.accumulate(va0, px);
+    D.scores(ka0, sx);
+    D.load_k(ring_k<P1>(), 1, ka1);
+    D.load_v(ring_v<P>(), 1, va1);
+    D.softmax(sy, py);
   };
-  for (int i = 0; i < my_nt; i += kSharedStages) {
-    body(std::integral_constant<int, 0>{}, i);
-    if (i + 1 >= my_nt) break;
-    body(std::integral_constant<int, 1>{}, i + 1);
-    if (i + 2 >= my_nt) break;
-    body(std::integral_constant<int, 2>{}, i + 2);
-    if (i + 3 >= my_nt) break;
-    body(std::integral_constant<int, 3>{}, i + 3);
-  }
+  for (int i = 0; i < my_nt; i += kSharedStages)
+    static_for<0, kSharedStages>([&](auto u) __attribute__((always_inline)) { body(u, i + decltype(u)::value); });
+  D.accumulate(va1, py);  // P V of the last unit
   // no direct load may still be writing this workgroup's LDS when its waves end
   wait_counts<0, 0>();
   asm volatile("" ::: "memory");
 
   const size_t pidx = (size_t)set * n_part + part;
-  const float lt = sum_across_halves(l[0]);
+  const float lt = sum_across_halves(D.lrow);
   const int rr = wave * 32 + l32;
   if (rc * kDecodeRows + rr >= p.rows) return;
   float* po = p.part_o + (pidx * kDecodeRows + rr) * kHeadDim;
@@ -479,11 +638,11 @@ __global__ __launch_bounds__(64 * NRB, 2) void decode_shared_kernel(DecodeParams
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = db * 32 + 8 * r4 + 4 * hl;
-      *(f32x4*)(po + d0) = f32x4{o[0][db][4 * r4], o[0][db][4 * r4 + 1], o[0][db][4 * r4 + 2], o[0][db][4 * r4 + 3]};
+      *(f32x4*)(po + d0) = f32x4{D.o[db][4 * r4], D.o[db][4 * r4 + 1], D.o[db][4 * r4 + 2], D.o[db][4 * r4 + 3]};
     }
   if (hl == 0) {
     float* pml = p.part_ml + pidx * 2 * kDecodeRows;
-    pml[rr] = m[0];
+    pml[rr] = D.mrow;
     pml[kDecodeRows + rr] = lt;
   }
 }
