@@ -4,28 +4,34 @@
 // Inference and Text Generation examples describe ("SnapKitty Transformer 8B").
 //
 // Bound.  Every visible K/V row of a kv head is read once for all of its H/G query heads
-// and Sq rows: at most 16 x 8 rows share a 64-key tile, i.e. at most ~8 k flop per byte
-// read, against a ridge near 300 for bf16 MFMA.  The pass is HBM-bound; the products
-// still run on MFMA (they are dense contractions over the head dimension and the keys)
-// so that the exps and the LDS traffic, not the arithmetic, are what remains per byte.
+// and Sq rows: at most 128 rows share a 64-key tile, i.e. at most 128 flop per byte read
+// (256 flop per row and key against 256 bytes of K and V per key), against a ridge near
+// 300 for bf16 MFMA.  The pass is HBM-bound, but at 128 rows its products and exps are
+// close to half of the stream's time, so they run on MFMA (dense contractions over the
+// head dimension and the keys) and overlap the loads.
 //
 // Work decomposition (split-KV).  The keys visible to at least one row (sink tiles, then
-// the window) form one list of 64-key tiles.  A workgroup of 4 waves serves one (batch,
-// kv head, chunk of up to 128 rows) and one of `nsplit` splits; each wave is an
-// independent partial that takes every (4 nsplit)-th tile of the list.  A wave streams
-// its tiles through its own two K/V buffers in LDS (direct loads, no registers, rows past
-// the cache read zero) and keeps an exact online softmax per row: the tile maximum, a
-// rescale of O and the row sum.  It writes its unnormalised O, maximum and sum; the merge
-// kernel combines the partials of each row with the log-sum-exp rule and writes O and lse.
-// Nothing is shared between waves, so there is no workgroup barrier; the buffers are
-// private to a wave and their loads are waited for with the wave's own counters.
+// the window) form one list of 64-key tiles, dealt round-robin to the partials of each
+// (batch, kv head, chunk of up to 128 rows); a merge kernel combines the partials of each
+// row with the log-sum-exp rule and writes O and lse.
+//  * Chunks of at most 32 rows: a workgroup of 4 waves, each wave an independent partial
+//    over every (4 nsplit)-th tile, streaming them through its own two K/V buffers in LDS
+//    (direct loads, rows past the cache read zero) and waiting with its own counters: no
+//    workgroup barrier.
+//  * Larger chunks: one wave per 32-row block, the workgroup one partial; its waves fill a
+//    5-stage LDS ring together and share every tile, one barrier per tile, and work in the
+//    prefill forward's unit pipeline (a unit's softmax beside the previous unit's P V and
+//    the next unit's scores).
+// Both keep an online softmax with the prefill forward's lazy maximum (a tile is
+// exponentiated against the running maximum unless a lane's partial row sum leaves its
+// guard) and write their unnormalised O, maximum and sum.
 //
 // Per wave and tile, as in the prefill forward: S^T = K Q^T on v_mfma_f32_32x32x16 with the
 // rows as the B operand held in registers (lane = row, so row statistics are in-lane plus
 // one exchange between the two 32-lane halves), P^T rounded to the 16-bit type feeds
 // O^T += V^T P^T from registers, and V^T comes from the row-major V tile through
-// ds_read_b64_tr_b16.  The K and V operands of a tile are read once and shared by the
-// (up to four) 32-row blocks.
+// ds_read_b64_tr_b16.  The K and V operands of a tile are read once per wave and shared by
+// its row blocks.
 #include <type_traits>
 
 #include "gqa_device.h"
