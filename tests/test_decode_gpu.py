@@ -37,8 +37,9 @@ def _check(w: DecodeWorkload):
 
 
 # (B, H, G, Sq, Skv, window, sinks, dtype): one key, ragged tails, 1..4 row blocks (rows =
-# H/G * Sq up to 128 per chunk), two row chunks, MHA, f16, Sq == Skv, a window that starts
-# inside the sinks' reach, many splits
+# H/G * Sq up to 128 per chunk: the shared-tile kernel with 2, 3 and 4 waves at 48, 72/84
+# and 112/128 rows), two row chunks, MHA, f16, Sq == Skv, a window that starts inside the
+# sinks' reach, many splits
 SMALL = [
     (1, 4, 2, 1, 1, 0, 0, "bf16"),
     (2, 8, 2, 3, 100, 0, 0, "bf16"),
@@ -51,6 +52,8 @@ SMALL = [
     (1, 8, 2, 4, 70000, 16384, 2048, "bf16"),
     (1, 12, 4, 3, 5000, 0, 0, "bf16"),
     (1, 4, 1, 2, 200, 130, 70, "bf16"),
+    (1, 16, 2, 6, 3000, 500, 16, "bf16"),
+    (1, 24, 2, 7, 2000, 0, 0, "f16"),
 ]
 
 
