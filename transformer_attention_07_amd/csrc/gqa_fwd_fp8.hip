@@ -38,6 +38,10 @@ typedef __attribute__((address_space(3))) void lds_void8;
 constexpr float kRescaleThreshold8 = 8.0f;  // log2 units: P <= 2^8 after the exact path
 constexpr float kSumGuard8 = 256.0f;        // a lane's partial row sum above this: exact path
 constexpr float kLn2_8 = 0.69314718055994530942f;
+// The running maximum of a row before its first visible key: finite and below every score
+// (log2 units), so the first visible key exponentiates to +inf and the row-sum guard takes
+// the exact path; masked keys (-inf) still give 0.
+constexpr float kNoMax8 = -1.0e38f;
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   // cbsz = blgp = 0: both operands e4m3; block scales 2^(127 - 127) = 1
@@ -135,9 +139,9 @@ struct Fp8Wave {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const float mnew = vmax(mrow[cb], mx[cb]);
-        alpha[cb] = mnew != -INFINITY ? exp2_fast(mrow[cb] - mnew) : 1.0f;
+        alpha[cb] = exp2_fast(mrow[cb] - mnew);  // finite: mrow starts at kNoMax8
         mrow[cb] = mnew;
-        nmuse[cb] = mnew == -INFINITY ? 0.f : -mnew;
+        nmuse[cb] = -mnew;
         lrow[cb] *= alpha[cb];
       }
       if constexpr (H == 1) {
@@ -181,8 +185,7 @@ struct Fp8Wave {
   __device__ __forceinline__ void softmax_half(const f32x16 (&s)[2], i32x8 (&pf)[2], const i32x8 (&va)[2]) {
     float ls[2];
     probs<H>(s, pf, ls);
-    const bool need = !(ls[0] <= kSumGuard8) | !(ls[1] <= kSumGuard8) | ((mrow[0] == -INFINITY) & (q0 + l32 < m.S)) |
-                      ((mrow[1] == -INFINITY) & (q0 + 32 + l32 < m.S));
+    const bool need = !(ls[0] <= kSumGuard8) | !(ls[1] <= kSumGuard8);
     if (__builtin_expect(wave_any(need), 0)) {
       decide<H>(s, pf, va);
       probs<H>(s, pf, ls);
@@ -284,10 +287,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) W.o[db][cb] = f32x16{};
-  W.mrow[0] = W.mrow[1] = -INFINITY;
+  W.mrow[0] = W.mrow[1] = kNoMax8;
   W.lrow[0] = W.lrow[1] = 0.f;
   W.alpha[0] = W.alpha[1] = 1.f;
-  W.nmuse[0] = W.nmuse[1] = 0.f;
+  W.nmuse[0] = W.nmuse[1] = -kNoMax8;
   W.lim_hi = __builtin_amdgcn_readfirstlane(W.m.causal ? imin(W.q0, S - 1) : S - 1);
   W.win_lo = __builtin_amdgcn_readfirstlane(W.m.window > 0 ? W.q1 - W.m.window + 1 : -(1 << 30));
   W.rescale = false;
