@@ -574,8 +574,8 @@ __global__ __launch_bounds__(64 * NRB, NRB > 2 ? 2 : 1) void decode_shared_kerne
   // read the scores of (i, 1) and (i + 1, 0), so tile i + 1 must have landed when tile
   // i starts: iteration i waits for this wave's loads of tile i + 1, then a barrier (every
   // wave's loads of tile i + 1 have landed; every wave is done with tile i - 1, whose
-  // second V half the previous unit read), then loads tile i + 4 into tile i - 1's
-  // buffer.  Three tiles are in flight during the wait.
+  // second V half the previous unit read), and at its end loads tile i + 4 into tile
+  // i - 1's buffer.  Three tiles are in flight during the wait.
   static_for<0, kSharedStages - 1>([&](auto u) __attribute__((always_inline)) {
     constexpr int U = decltype(u)::value;
     stage(ring_k<U>(), ring_v<U>(), tile_row(U));
@@ -600,7 +600,9 @@ __global__ __launch_bounds__(64 * NRB, NRB > 2 ? 2 : 1) void decode_shared_kerne
 
   // Step i: the wait, barrier and loads run on every step of the last round too (past the
   // end they load zeros, with no memory traffic), so that every path through the loop has
-  // the same loads in flight; only the units are skipped past the last tile.
+  // the same loads in flight; only the units are skipped past the last tile.  The loads go
+  // at the step's end, after its LDS reads (issued right before them, they made the
+  // compiler wait for every load in flight ahead of one of the reads).
   auto body = [&](auto par, int i) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     constexpr int P1 = (P + 1) % kSharedStages;                  // tile i + 1
@@ -609,8 +611,10 @@ __global__ __launch_bounds__(64 * NRB, NRB > 2 ? 2 : 1) void decode_shared_kerne
     wait_counts<(kSharedStages - 3) * kMinPerTile, 0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    stage(ring_k<F>(), ring_v<F>(), tile_row(i + kSharedStages - 1));
-    if (i >= my_nt) return;
+    if (i >= my_nt) {
+      stage(ring_k<F>(), ring_v<F>(), tile_row(i + kSharedStages - 1));
+      return;
+    }
     const int k0 = tile_row(i);
     // (i, 0) from sx; P V of (i - 1, 1); scores of (i, 1)
     if (__builtin_expect(!half_full(k0), 0)) D.mask(sx, k0, Skv, W, NS);
@@ -626,6 +630,7 @@ __global__ __launch_bounds__(64 * NRB, NRB > 2 ? 2 : 1) void decode_shared_kerne
     D.load_k(ring_k<P1>(), 1, ka1);
     D.load_v(ring_v<P>(), 1, va1);
     D.softmax(sy, py);
+    stage(ring_k<F>(), ring_v<F>(), tile_row(i + kSharedStages - 1));
   };
   for (int i = 0; i < my_nt; i += kSharedStages)
     static_for<0, kSharedStages>([&](auto u) __attribute__((always_inline)) { body(u, i + decltype(u)::value); });
