@@ -693,7 +693,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) mg = vmax(mg, __shfl_xor(mg, s, 64));
     const float mnew = vmax(mrun, mg);
-    // a partial (or the groups so far) with no visible key has maximum -inf and weight 0
+    // a partial (or the groups so far) with no visible key has maximum -inf (the
+    // shared-tile kernel's: -1e38) and weight 0
     const float keep = mrun == -INFINITY ? 0.f : exp2_fast(mrun - mnew);
     const float w = mi == -INFINITY ? 0.f : exp2_fast(mi - mnew);
     float wl = w * li;

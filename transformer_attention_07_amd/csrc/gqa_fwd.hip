@@ -22,9 +22,10 @@
 // Online softmax in fp32: exp2 with scale*log2(e) folded into one FMA and row sums of the
 // unrounded P in fp32 (so lse keeps fp32 accuracy).  The running maximum only keeps exp2
 // in range, so a unit is exponentiated against it without computing the unit's own
-// maximum; a lane's partial row sum above 2^16 (or a row with no maximum yet) sends the
-// unit through the exact path: take its maximum, raise the running maximum when it grew by
-// more than 2^8, rescale O and the sums, exponentiate again.  P thus stays below 2^16,
+// maximum; a lane's partial row sum above 2^16 (a row's first visible key always gives
+// one, against the finite starting maximum) sends the unit through the exact path: take
+// its maximum, raise the running maximum when it grew by more than 2^8, rescale O and the
+// sums, exponentiate again.  P thus stays below 2^16,
 // which the rounded operands and fp32 sums carry at full relative precision.  Units that
 // are not fully visible are masked with one compare per element against per-lane bounds.
 //
