@@ -314,4 +314,30 @@ __device__ __forceinline__ u32x4 rope_chunk16(u32x4 w, int pos, const double (&r
   return w;
 }
 
+// Which (row block, head group) a forward workgroup serves (bf16 and FP8 forwards alike:
+// Params has n_qblk, B, H, hpw, xcd_hg, xcd_kv).  Longest row blocks first in both
+// orders.  Workgroup j runs on XCD j mod 8; in the plain order consecutive workgroups take
+// consecutive head groups, so an XCD serves every eighth head group and a kv head's K/V
+// tiles pass through two XCDs' L2 caches.  With xcd_hg > 0 (B * H / hpw a multiple of 8,
+// each XCD's share of whole kv heads) XCD x serves head groups x * xcd_hg .. + xcd_hg - 1,
+// one row block of each after the other: fewer kv heads per L2 at any time.
+template <class Params>
+__device__ __forceinline__ void fwd_block_order(const Params& p, int j, int& qblk, int& rest) {
+  if (p.xcd_hg > 0 && p.xcd_kv > 0) {
+    const int x = j & 7, pos = j >> 3;
+    const int per_kv = p.n_qblk * p.xcd_kv;  // workgroups of one kv head
+    const int kvi = pos / per_kv, r = pos % per_kv;
+    qblk = p.n_qblk - 1 - r / p.xcd_kv;
+    rest = x * p.xcd_hg + kvi * p.xcd_kv + r % p.xcd_kv;
+  } else if (p.xcd_hg > 0) {
+    const int x = j & 7, pos = j >> 3;
+    qblk = p.n_qblk - 1 - pos / p.xcd_hg;
+    rest = x * p.xcd_hg + pos % p.xcd_hg;
+  } else {
+    const int per_q = p.B * (p.H / p.hpw);
+    qblk = p.n_qblk - 1 - j / per_q;
+    rest = j % per_q;
+  }
+}
+
 }  // namespace gqa

@@ -245,30 +245,6 @@ __device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t rs, char* tile
                                              row0 * 128 + voff[u], 0, 0, 0);
 }
 
-// Which (row block, head group) a workgroup serves.  Longest row blocks first in both
-// orders.  Workgroup j runs on XCD j mod 8; in the plain order consecutive workgroups take
-// consecutive head groups, so an XCD serves every eighth head group and a kv head's K/V
-// tiles pass through two XCDs' L2 caches.  With xcd_hg > 0 (B * H / hpw a multiple of 8,
-// each XCD's share of whole kv heads) XCD x serves head groups x * xcd_hg .. + xcd_hg - 1,
-// one row block of each after the other: fewer kv heads per L2 at any time.
-__device__ __forceinline__ void fwd_block_order(const FwdParams& p, int j, int& qblk, int& rest) {
-  if (p.xcd_hg > 0 && p.xcd_kv > 0) {
-    const int x = j & 7, pos = j >> 3;
-    const int per_kv = p.n_qblk * p.xcd_kv;  // workgroups of one kv head
-    const int kvi = pos / per_kv, r = pos % per_kv;
-    qblk = p.n_qblk - 1 - r / p.xcd_kv;
-    rest = x * p.xcd_hg + kvi * p.xcd_kv + r % p.xcd_kv;
-  } else if (p.xcd_hg > 0) {
-    const int x = j & 7, pos = j >> 3;
-    qblk = p.n_qblk - 1 - pos / p.xcd_hg;
-    rest = x * p.xcd_hg + pos % p.xcd_hg;
-  } else {
-    const int per_q = p.B * (p.H / p.hpw);
-    qblk = p.n_qblk - 1 - j / per_q;
-    rest = j % per_q;
-  }
-}
-
 template <int DT, bool ROPE>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_lds0[8192];

@@ -237,9 +237,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int nhq = p.H / p.hpw;
-  const int per_q = p.B * nhq;
-  const int qblk = p.n_qblk - 1 - (int)(blockIdx.x / per_q);
-  const int rest = (int)(blockIdx.x % per_q);
+  int qblk, rest;  // row block and head group (b * nhq + head block) of this workgroup
+  fwd_block_order(p, (int)blockIdx.x, qblk, rest);
   const int b = rest / nhq;
   const int h = (rest % nhq) * p.hpw + (wave % p.hpw);
   const int g = h / (p.H / p.G);

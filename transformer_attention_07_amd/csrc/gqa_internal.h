@@ -243,6 +243,7 @@ struct Fp8FwdParams {
   float o_scale;     // V's dequantisation factor
   MaskSpec mask;
   int hpw, qpw, n_qblk;
+  int xcd_hg, xcd_kv;  // workgroup order, as FwdParams
 };
 
 struct VtParams {
