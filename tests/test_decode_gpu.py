@@ -7,6 +7,8 @@ row blocks and row chunks with ragged tails, and at the two full-size decode wor
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -92,6 +94,29 @@ def test_decode_maximum_jumps_inside_tiles(sq):
     k[:, :, 64:96] = 2.0
     k[:, :, 96:128] = 4.0
     v = torch.randn((B, G, Skv, 64), generator=torch.Generator().manual_seed(7320))
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    o, lse = gqa.gqa_attn_decode(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    O, L = ref.decode(q, k, v)
+    eo = np.abs(o.float().cpu().numpy().astype(np.float64) - O)
+    el = np.abs(lse.cpu().numpy().astype(np.float64) - L)
+    print(f"  O: max {eo.max():.3e} mean {eo.mean():.3e}; lse: max {el.max():.3e}", flush=True)
+    assert np.isfinite(eo).all() and np.isfinite(el).all()
+    assert eo.max() <= O_MAX and eo.mean() <= O_MEAN and el.max() <= LSE_MAX
+
+
+@pytest.mark.parametrize("sq", [1, 16])
+def test_decode_first_keys_far_below_the_rest(sq):
+    # the first 64 cache keys score about -1000 (log2 units), keys 160..223 about +23: the
+    # partials that hold only low keys keep a maximum near -1000 and get merge weight 0, the
+    # others raise theirs by ~1000 and scale what came before by exactly 0
+    B, H, G, Skv = 1, 8, 1, 320
+    c = 1000.0 / (2.0 * 64 * (64 ** -0.5) * math.log2(math.e))
+    q = torch.full((B, H, sq, 64), 2.0)
+    k = torch.zeros((B, G, Skv, 64))
+    k[:, :, :64] = -c
+    k[:, :, 160:224] = 1.0
+    v = torch.randn((B, G, Skv, 64), generator=torch.Generator().manual_seed(7333))
     q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
     o, lse = gqa.gqa_attn_decode(q.cuda(), k.cuda(), v.cuda())
     torch.cuda.synchronize()

@@ -174,3 +174,22 @@ def test_fp8_maximum_jump_inside_a_tile():
     o, lse = _run(w, q8, k8, v8, sc)
     rows = np.array([(0, h, i) for h in range(2) for i in range(S)])
     _check_rows(w, rows, q8, k8, v8, sc, o, lse)
+
+
+def test_fp8_first_keys_far_below_the_rest():
+    # Keys 0..63 score about -1000 (log2 units), keys 64..95 zero, 96..159 about +23: rows
+    # 0..63 leave the running maximum's start on their first visible key; at tile 1 later
+    # rows raise it by ~1000 in the first half (scaling O by exactly 0) and again in the
+    # second half while the first half's P waits in its operand.
+    S = 192
+    w = Workload("fp8_far_below", B=1, H=2, G=1, S=S, causal=True, seed=7340)
+    q = torch.full((1, 2, S, 64), 2.0)
+    k = torch.zeros((1, 1, S, 64))
+    k[0, 0, :64] = -44.0    # e4m3-exact; log2 score 2 * 64 * -44 * 0.125 * log2(e) = -1016
+    k[0, 0, 96:160] = 1.0
+    v = torch.randn((1, 1, S, 64), generator=torch.Generator().manual_seed(7341))
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn) for x in (q, k, v))
+    sc = (1.0, 1.0, 1.0)
+    o, lse = _run(w, q8, k8, v8, sc)
+    rows = np.array([(0, h, i) for h in range(2) for i in range(S)])
+    _check_rows(w, rows, q8, k8, v8, sc, o, lse)

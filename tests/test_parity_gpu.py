@@ -16,6 +16,7 @@ thread each); that only changes which core computes a row, not its arithmetic.
 from __future__ import annotations
 
 import json
+import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -375,6 +376,28 @@ def _jump_inputs(B, H, G, S, dtype=torch.bfloat16, seed=7311):
     k[:, :, 96:128] = 4.0
     v = torch.randn((B, G, S, 64), generator=torch.Generator().manual_seed(seed))
     return tuple(x.to(dtype) for x in (q, k, v))
+
+
+def test_first_keys_far_below_the_rest():
+    # The first 64 keys score about -1000 (log2 units), the keys from 96 on about +23: rows
+    # 0..63 see only the low keys (their first visible key leaves the running maximum's
+    # start through the exact path), later rows see both, and raising the maximum by ~1000
+    # scales what came before by exactly 0.  Every score is exact enough in fp32.  (Forward
+    # only: the backward keeps no running maximum, and for rows 0..63 its dQ is a sum of
+    # rounded dS against one constant K row of size 43, whose exact value 0 no 16-bit dS
+    # reaches within the stated bar.)
+    w = Workload("far_below", B=1, H=2, G=1, S=192, direction="fwd", seed=7330)
+    c = 1000.0 / (2.0 * 64 * w.scale * math.log2(math.e))  # q = 2: log2 score = -2 * 64 * c * scale * log2 e
+    q = torch.full((w.B, w.H, w.S, 64), 2.0)
+    k = torch.zeros((w.B, w.G, w.S, 64))
+    k[:, :, :64] = -c
+    k[:, :, 96:160] = 1.0
+    v = torch.randn((w.B, w.G, w.S, 64), generator=torch.Generator().manual_seed(7331))
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    _, o, lse = run_fwd(w, q, k, v)
+    O, L = ref.forward(q, k, v, scale=w.scale, causal=True)
+    _err("O", _np(o), O, LP_MAX, LP_MEAN)
+    _err("lse", _np(lse), L, LSE_MAX)
 
 
 def test_maximum_jumps_inside_tiles():
